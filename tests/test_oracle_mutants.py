@@ -1,0 +1,89 @@
+"""Planted mistakes in (a copy of) the oracle must each fail at least one pin.
+
+Each mutant rewrites one line of the oracle's source (a dropped term, a wrong
+sign or index, a transposed operand, a wrong mask or log base), loads it as a
+separate module, swaps it in, and runs the pins from ``test_oracle.py``.
+"""
+import inspect
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as A
+from oracle import zigzag as Z
+from tests import test_oracle as T
+
+MUTANTS = {
+    "strict_causal": ("pos_k[None, :] <= pos_q[:, None]", "pos_k[None, :] < pos_q[:, None]"),
+    "no_scale_in_scores": ("s = scale * (qb @ kc.T)", "s = (qb @ kc.T)"),
+    "log2_lse": ("m + np.log(np.where(has, l, 1.0))", "m + np.log2(np.where(has, l, 1.0))"),
+    "delta_sign": ("ds = p * (dp - dl[:, None])", "ds = p * (dp + dl[:, None])"),
+    "dq_no_scale": ("dq[i0:i1] = scale * (ds @ kc)", "dq[i0:i1] = (ds @ kc)"),
+    "dk_uses_p": ("dk[cols] += scale * (ds.T @ q[i0:i1])", "dk[cols] += scale * (p.T @ q[i0:i1])"),
+    "dv_uses_ds": ("dv[cols] += p.T @ dob", "dv[cols] += ds.T @ dob"),
+    "delta_from_v": ("dl = np.sum(dob * ob, axis=1)", "dl = np.sum(dob * dob, axis=1)"),
+    "merge_swapped": ("w1 * o1 + w2 * o2", "w2 * o1 + w1 * o2"),
+    "merge_no_log": ("lse = np.logaddexp(lse1, lse2)", "lse = np.maximum(lse1, lse2)"),
+    "pv_transposed_v": ("o = p @ vc", "o = p @ vc[::-1]"),
+}
+
+ZMUTANTS = {
+    "zigzag_wrong_partner": ("chunk_positions(2 * world - 1 - rank, C)", "chunk_positions(2 * world - 2 - rank, C)"),
+    "zigzag_swapped_order": ("[chunk_positions(rank, C), chunk_positions(2 * world - 1 - rank, C)]",
+                             "[chunk_positions(2 * world - 1 - rank, C), chunk_positions(rank, C)]"),
+}
+
+PINS = [
+    lambda: T.test_golden_attention("causal_two_tokens.json"),
+    lambda: T.test_golden_attention("full_one_query.json"),
+    T.test_golden_merge,
+    lambda: T.test_bruteforce_tiny(1, True, "random"),
+    lambda: T.test_torch_autograd(0, True, 4),
+    T.test_zero_query_counts_and_means,
+    lambda: T.test_split_merge_equals_unsplit("random", True),
+]
+
+ZPINS = [
+    T.test_golden_zigzag,
+    lambda: T.test_zigzag_reassembles_causal_attention(3, 5),
+]
+
+
+def _load_mutant(module, old, new):
+    src = inspect.getsource(module)
+    assert src.count(old) == 1, old
+    mod = types.ModuleType(module.__name__ + "_mutant")
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+def _fails(pins):
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed += 1
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_attention_mutant_is_caught(name, monkeypatch):
+    mod = _load_mutant(A, *MUTANTS[name])
+    for fn in ("allowed_mask", "attn_fwd", "attn_bwd", "lse_merge", "_block_fwd"):
+        monkeypatch.setattr(A, fn, getattr(mod, fn))
+    with np.errstate(all="ignore"):
+        assert _fails(PINS) >= 1, f"no pin caught mutant {name}"
+
+
+@pytest.mark.parametrize("name", sorted(ZMUTANTS))
+def test_zigzag_mutant_is_caught(name, monkeypatch):
+    mod = _load_mutant(Z, *ZMUTANTS[name])
+    monkeypatch.setattr(oracle, "zigzag_positions", mod.zigzag_positions)
+    assert _fails(ZPINS) >= 1, f"no pin caught mutant {name}"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert _fails(PINS + ZPINS) == 0
