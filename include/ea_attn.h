@@ -1,0 +1,187 @@
+/*
+ * ea_attn: blockwise causal attention (forward, backward, LSE merge) for one
+ * sequence-parallel rank's share of a long sequence, on AMD MI355X (gfx950).
+ *
+ * The operations follow the EasyContext pages:
+ *  - ring attention cuts one sequence over GPUs; each rank attends its local
+ *    queries to one rank's key/value share per ring step and combines the
+ *    partial results (EasyContext core-technology page, hotelren.com,
+ *    section 1 "sequence parallelism");
+ *  - the zigzag ring mode interleaves tokens across ranks (EasyContext
+ *    training-script walkthrough, mlqm.cn, section on model preparation and
+ *    parallel strategies);
+ *  - each rank's shard carries its global position ids (EasyContext
+ *    "1M tokens with minimal resources" page, cn486.com, usage code);
+ *  - the per-block attention is the tiled Flash Attention forward and its
+ *    recompute-based backward (hotelren.com page, section 2 "Flash Attention
+ *    optimisation").
+ * No formula is printed on the pages; the definitions used are stated with
+ * each call below.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  Layout.  Per-token tensors are [B, S, H, D] row-major with D contiguous:
+ *    element (b, i, h, d) lives at ((b * batch_rows + i) * H + h) * D + d,
+ *    where batch_rows (>= S) is the row stride between batches, so a
+ *    contiguous row sub-range of a larger buffer is passed as a pointer offset
+ *    with the parent's batch_rows.  Per-row statistics (LSE, Delta) are
+ *    [B, S, H] fp32 at ((b * batch_rows + i) * H + h).
+ *  Types.  q, k, v, dout are bf16 (stored as uint16_t).  o is fp32 or bf16
+ *    (o_dtype / part_dtype: EA_F32 or EA_BF16).  lse, delta, dq, dk, dv are fp32.
+ *  Positions.  Token i of a tensor has a global integer position given by at
+ *    most two segments: seg = {start0, len0, start1, len1} (n_seg = 2) or
+ *    {start0, len0} (n_seg = 1); rows [0, len0) have positions start0 + i, rows
+ *    [len0, len0 + len1) have positions start1 + (i - len0).  The lengths must
+ *    sum to the tensor's row count, starts must be >= 0 and every position
+ *    < 2^31.  Segment arrays are host memory, read during the call only.
+ *  Mask.  EA_MASK_FULL allows every (query, key) pair; EA_MASK_CAUSAL allows
+ *    key j for query i iff pos_k(j) <= pos_q(i) (the diagonal is kept).
+ *  Scale.  scale multiplies <q_i, k_j>; it must be finite and > 0.
+ *  Sizes.  B, H >= 1; D in {64, 128}; S >= 0 and < 2^31.
+ *  Alignment.  q, k, v, o, dout and o_part must be 16-byte aligned; fp32
+ *    arrays 4-byte aligned.
+ *  Ownership.  The caller owns every buffer (device memory, except the
+ *    segment arrays).  The library allocates nothing and keeps no state on the
+ *    device.  Inputs are read-only; outputs may not overlap inputs (except the
+ *    in-place accumulators of ea_lse_merge).
+ *  Streams.  `stream` is a hipStream_t (NULL = the default stream).  All work
+ *    is enqueued on it and the call returns without synchronising; buffers
+ *    must stay alive until the stream passes the call.  Calls that write the
+ *    same buffers must be ordered on one stream.
+ *  Errors.  Every call returns EA_OK (0) or a positive code.  Argument errors
+ *    (EA_ERR_NULL ... EA_ERR_ALIAS) are found on the host before any HIP call
+ *    is made, and nothing is enqueued.  EA_ERR_HIP means a launch failed; the
+ *    HIP message is then available from ea_last_hip_error() (per thread).  No
+ *    call aborts, throws or synchronises the device.
+ */
+#ifndef EA_ATTN_H
+#define EA_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum ea_status {
+  EA_OK = 0,
+  EA_ERR_NULL = 1,         /* a required pointer is NULL */
+  EA_ERR_SHAPE = 2,        /* B, H, S, batch_rows out of range */
+  EA_ERR_UNSUPPORTED = 3,  /* D, dtype, mask mode or scale not supported */
+  EA_ERR_POSITIONS = 4,    /* bad segment count, lengths, starts or positions >= 2^31 */
+  EA_ERR_ALIGN = 5,        /* pointer misaligned */
+  EA_ERR_ALIAS = 6,        /* an output overlaps an input */
+  EA_ERR_HIP = 7           /* a HIP launch failed */
+};
+
+enum ea_mask { EA_MASK_FULL = 0, EA_MASK_CAUSAL = 1 };
+enum ea_dtype { EA_F32 = 0, EA_BF16 = 1 };
+
+/*
+ * Forward.  For every (b, query row i, head h):
+ *   S_ij  = scale * <q_i, k_j> for allowed pairs,
+ *   LSE_i = ln sum_j exp(S_ij)            (natural log; -inf if no key is allowed),
+ *   O_i   = sum_j exp(S_ij - LSE_i) v_j    (0 if no key is allowed).
+ * q [B,Sq,H,D], k and v [B,Sk,H,D] (bf16); writes o [B,Sq,H,D] in o_dtype and
+ * lse [B,Sq,H] (fp32).  Sq == 0 does nothing; Sk == 0 writes O = 0, LSE = -inf.
+ * This is one ring step's partial result when k/v hold one rank's share.
+ */
+int ea_attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+                int B, int H, int64_t Sq, int64_t Sk, int D,
+                int64_t q_batch_rows, int64_t k_batch_rows,
+                const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg,
+                int mask_mode, float scale, void* stream);
+
+/*
+ * Backward by recomputation from the saved statistics (the recompute-and-tile
+ * gradient of the hotelren.com page, section 2).  With P_ij =
+ * exp(scale*<q_i,k_j> - LSE_i) on allowed pairs (0 elsewhere):
+ *   Delta_i = <dout_i, o_i>
+ *   dS_ij   = P_ij (<dout_i, v_j> - Delta_i)
+ *   dq_i   += scale * sum_j dS_ij k_j
+ *   dk_j   += scale * sum_i dS_ij q_i
+ *   dv_j   += sum_i P_ij dout_i
+ * dq [B,Sq,H,D], dk and dv [B,Sk,H,D] are fp32 and ACCUMULATED (+=): zero them
+ * before the first call.  lse and o must be the FINAL statistics of the query
+ * rows over all keys they attend to (for a ring: the merged result), so that
+ * the per-step calls sum to the gradient of the whole attention.
+ * delta [B,Sq,H] fp32: if delta_ready == 0 the call first computes Delta from
+ * o and dout into it; otherwise it is read as given (compute it once per ring,
+ * then pass delta_ready = 1).  Rows whose lse is -inf contribute nothing.
+ * Sq == 0 or Sk == 0 leaves the accumulators unchanged (Delta is still
+ * written when Sq > 0 and delta_ready == 0).
+ */
+int ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                const void* dout, const float* lse, float* delta, int delta_ready,
+                float* dq, float* dk, float* dv,
+                int B, int H, int64_t Sq, int64_t Sk, int D,
+                int64_t q_batch_rows, int64_t k_batch_rows,
+                const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg,
+                int mask_mode, float scale, void* stream);
+
+/*
+ * In-place LSE merge of a partial result over a disjoint key set into an
+ * accumulator (ring attention combines one step's partial per rank visited):
+ *   L   = ln(exp(lse_acc) + exp(lse_part))
+ *   o_acc = exp(lse_acc - L) * o_acc + exp(lse_part - L) * o_part,  lse_acc = L.
+ * A side whose LSE is -inf contributes nothing; both -inf gives (0, -inf).
+ * o_acc [B,Sq,H,D] fp32, lse_acc [B,Sq,H]; o_part in part_dtype, lse_part fp32;
+ * all with row stride q_batch_rows between batches.
+ */
+int ea_lse_merge(float* o_acc, float* lse_acc, const void* o_part, int part_dtype,
+                 const float* lse_part, int B, int H, int64_t Sq, int D,
+                 int64_t q_batch_rows, void* stream);
+
+/*
+ * Host-only helper (no HIP call): position segments of one rank's share in a
+ * zigzag ring.  The sequence of s_total tokens is cut into 2*world equal
+ * chunks of C tokens; rank r holds chunk r followed by chunk 2*world-1-r
+ * (reading of the mlqm.cn walkthrough's zigzag mode: interleaving an early and
+ * a late chunk balances causal work across ranks).  Writes
+ * seg_out[4] = {r*C, C, (2*world-1-r)*C, C}.  Returns EA_ERR_POSITIONS if
+ * s_total is not a positive multiple of 2*world, rank is out of range, or a
+ * position would reach 2^31; EA_ERR_NULL for a NULL seg_out.
+ */
+int ea_zigzag_segments(int64_t s_total, int world, int rank, int64_t* seg_out);
+
+/* Host-only helper: the rank whose key/value share rank `rank` holds at ring
+ * step `step` of `world` ranks: (rank - step) mod world.  Returns -1 for
+ * out-of-range arguments. */
+int ea_ring_source(int rank, int step, int world);
+
+/*
+ * Per-kernel timing (diagnostics).  Between ea_profile_begin() and
+ * ea_profile_end() every kernel the library launches (on any stream) is
+ * bracketed by a pair of HIP events recorded on its stream.  Recording adds
+ * two event records per launch and no synchronisation.  ea_profile_query()
+ * waits for the recorded events of one kernel kind and returns the summed
+ * device time in milliseconds and the number of launches since the last
+ * ea_profile_begin().  Kernel kinds are the EA_KERNEL_* values;
+ * ea_kernel_name() gives their names.  Returns EA_OK, EA_ERR_UNSUPPORTED for a
+ * bad kind, EA_ERR_NULL for NULL outputs, or EA_ERR_HIP.  Profiling state is
+ * process-wide and guarded by a lock.
+ */
+enum ea_kernel {
+  EA_KERNEL_FWD = 0,
+  EA_KERNEL_BWD_DELTA = 1,
+  EA_KERNEL_BWD_DKDV = 2,
+  EA_KERNEL_BWD_DQ = 3,
+  EA_KERNEL_LSE_MERGE = 4,
+  EA_KERNEL_COUNT = 5
+};
+int ea_profile_begin(void);
+int ea_profile_end(void);
+int ea_profile_query(int kernel, double* total_ms, int64_t* launches);
+const char* ea_kernel_name(int kernel);
+
+const char* ea_strerror(int status);
+/* Text of the last HIP error seen by an EA_ERR_HIP return on this thread. */
+const char* ea_last_hip_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int ea_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EA_ATTN_H */

@@ -1,0 +1,103 @@
+// Device-side building blocks shared by the gfx950 attention kernels:
+// vector types, the bf16 MFMA wrappers, global-position segments and the
+// XCD-aware work mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ea {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Lane l supplies row (l % 32) of A and column (l % 32) of B, each holding the
+// 8 reduction indices 8*(l/32) .. 8*(l/32)+7 of the 16.  Output register r of
+// lane l holds D[8*(r/4) + 4*(l/32) + r%4][l % 32].
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(float x0, float x1, float x2, float x3, float x4, float x5,
+                                              float x6, float x7) {
+  u32x4 u;
+  u[0] = pack_bf16x2(x0, x1);
+  u[1] = pack_bf16x2(x2, x3);
+  u[2] = pack_bf16x2(x4, x5);
+  u[3] = pack_bf16x2(x6, x7);
+  return as_bf16x8(u);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Exponent base 2 on the hardware transcendental unit.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Global positions of the rows of one tensor: rows [0, l0) sit at s0 + i, rows
+// [l0, n) at s1 + (i - l0).  A single-segment tensor has l0 = n.
+struct Seg {
+  int s0, l0, s1, n;
+};
+
+__device__ __forceinline__ int seg_pos(const Seg& g, int i) { return i < g.l0 ? g.s0 + i : g.s1 + (i - g.l0); }
+
+// Smallest and largest position among rows [a, b) (a < b <= n).
+__device__ __forceinline__ void seg_range(const Seg& g, int a, int b, int& mn, int& mx) {
+  mn = 0x7fffffff;
+  mx = -1;
+  if (a < g.l0) {
+    int e = b < g.l0 ? b : g.l0;
+    mn = g.s0 + a;
+    mx = g.s0 + e - 1;
+  }
+  if (b > g.l0) {
+    int st = a > g.l0 ? a : g.l0;
+    int p0 = g.s1 + (st - g.l0), p1 = g.s1 + (b - 1 - g.l0);
+    mn = p0 < mn ? p0 : mn;
+    mx = p1 > mx ? p1 : mx;
+  }
+}
+
+// Key rows that any query with position <= qmax may see under the causal rule,
+// as up to two row ranges [0, e0) and [b1, e1) of the key tensor.
+__device__ __forceinline__ void causal_key_ranges(const Seg& k, int qmax, int& e0, int& b1, int& e1) {
+  long n0 = (long)qmax - k.s0 + 1;
+  n0 = n0 < 0 ? 0 : (n0 > k.l0 ? k.l0 : n0);
+  e0 = (int)n0;
+  long len1 = k.n - k.l0;
+  long n1 = (long)qmax - k.s1 + 1;
+  n1 = n1 < 0 ? 0 : (n1 > len1 ? len1 : n1);
+  b1 = k.l0;
+  e1 = k.l0 + (int)n1;
+}
+
+enum TileClass { kSkip = 0, kFull = 1, kPartial = 2 };
+
+// Hardware places workgroup `bid` on XCD bid % 8.  Give each XCD a contiguous
+// slice of the work list so that neighbouring work items (same batch and head,
+// hence the same keys/values) share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+  int xcd = bid % kNumXcd, slot = bid / kNumXcd;
+  int per = nwg / kNumXcd, rem = nwg % kNumXcd;
+  int start = xcd * per + (xcd < rem ? xcd : rem);
+  return start + slot;
+}
+
+}  // namespace ea

@@ -1,0 +1,64 @@
+// Host-side launch parameters and launchers of the gfx950 kernels.  The public
+// C entry points (api.hip) validate their arguments, fill these structs and
+// call the launchers; nothing here checks arguments again.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ea {
+
+struct SegArg {
+  int s0, l0, s1, n;  // rows [0,l0) at s0+i, rows [l0,n) at s1+(i-l0)
+};
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* o;
+  float* lse;
+  int B, H, D, Sq, Sk;
+  int64_t q_batch_rows, k_batch_rows;
+  SegArg qs, ks;
+  int causal;
+  int o_bf16;
+  float scale;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const void* o;
+  const uint16_t* dout;
+  const float* lse;
+  float* delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  int B, H, D, Sq, Sk;
+  int64_t q_batch_rows, k_batch_rows;
+  SegArg qs, ks;
+  int causal;
+  int o_bf16;
+  float scale;
+};
+
+struct MergeArgs {
+  float* o_acc;
+  float* lse_acc;
+  const void* o_part;
+  const float* lse_part;
+  int part_bf16;
+  int B, H, D, Sq;
+  int64_t q_batch_rows;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+}  // namespace ea

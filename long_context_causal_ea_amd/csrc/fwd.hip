@@ -1,0 +1,326 @@
+// Forward kernel: tiled attention with online softmax and LSE output
+// (EasyContext core-technology page, hotelren.com, section 2 "Flash Attention
+// optimisation": the attention matrix is never stored; key/value tiles are
+// staged on chip and the softmax is accumulated tile by tile).
+//
+// gfx950 mapping
+//  - One workgroup = 4 waves = 128 query rows of one (batch, head); each wave
+//    owns 32 rows.  Key/value tiles of 64 rows stream through LDS, double
+//    buffered, with the next tile's global loads in flight during compute.
+//  - Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
+//    every lane then holds 32 scores of ONE query row, so the row max and row
+//    sum are in-lane reductions plus one exchange with lane l^32.
+//  - P^T (bf16, round-to-nearest-even) feeds O^T += V^T P^T directly from
+//    registers; V is stored transposed in LDS so that the MFMA's reduction
+//    index (keys) is contiguous for each lane.
+//  - exp is computed as exp2 with scale*log2(e) folded into one FMA.
+//  - Tiles are classified per wave from global positions: SKIP (no allowed
+//    pair), FULL (all allowed, no mask work) or PARTIAL (element mask; also
+//    ragged key tails).  Tiles no query of the workgroup may see are never
+//    loaded.
+#include "ea_device.h"
+#include "ea_launch.h"
+
+namespace ea {
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* o;
+  float* lse;
+  long q_bstride, k_bstride, lse_bstride;  // elements between batches
+  long rs;                                 // row stride (H*D elements)
+  int H, Sq, Sk, nqb;
+  Seg qs, ks;
+  int causal, o_bf16;
+  float scale, c;  // c = scale * log2(e)
+};
+
+template <int D>
+struct FwdCfg {
+  static constexpr int BQ = 128, BK = 64, NT = 256;
+  static constexpr int KP = D + 8;   // Ks row stride (elements): 16-byte skew per row
+  static constexpr int VP = BK + 8;  // Vt row stride
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  static constexpr int NKL = BK * CPR / NT;
+  static constexpr int NVU = (BK / 4) * CPR;  // transposing units (4 keys x 8 dims)
+  static constexpr int LDS_K = BK * KP, LDS_V = D * VP;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
+  using Cfg = FwdCfg<D>;
+  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, KP = Cfg::KP, VP = Cfg::VP, CPR = Cfg::CPR;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][Cfg::LDS_K];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][Cfg::LDS_V];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ln = lane & 31, g = lane >> 5;
+
+  // ---- work item: (batch*head) major, longest query blocks first
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = work / p.nqb;
+  const int qb = p.nqb - 1 - work % p.nqb;
+  const int b = bh / p.H, h = bh % p.H;
+  const int D_ = D;
+
+  const uint16_t* qp = p.q + b * p.q_bstride + (long)h * D_;
+  const uint16_t* kp = p.k + b * p.k_bstride + (long)h * D_;
+  const uint16_t* vp = p.v + b * p.k_bstride + (long)h * D_;
+
+  const int i0 = qb * BQ;
+  const int qrow = i0 + w * 32 + ln;
+  const bool row_ok = qrow < p.Sq;
+
+  // ---- this lane's query row in MFMA B-operand form (8 dims per k-step)
+  bf16x8 qf[NKS];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(qp + (long)(row_ok ? qrow : 0) * p.rs + 8 * g);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 u = row_ok ? src[2 * ks] : u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = as_bf16x8(u);
+    }
+  }
+  const int qpos = seg_pos(p.qs, row_ok ? qrow : (p.Sq - 1));
+
+  // ---- position ranges of the workgroup's and this wave's valid rows
+  const int wg_end = min(i0 + BQ, p.Sq);
+  int qmin_wg, qmax_wg;
+  seg_range(p.qs, i0, wg_end, qmin_wg, qmax_wg);
+  const int w0 = i0 + w * 32, w1 = min(w0 + 32, p.Sq);
+  const bool wave_live = w0 < w1;
+  int qmin_w = 0, qmax_w = -1;
+  if (wave_live) seg_range(p.qs, w0, w1, qmin_w, qmax_w);
+
+  // ---- key tiles to visit: up to two contiguous runs
+  int e0 = p.Sk, b1 = p.Sk, e1 = p.Sk;
+  if (p.causal) causal_key_ranges(p.ks, qmax_wg, e0, b1, e1);
+  const int nA = (e0 + BK - 1) / BK;
+  int tB0 = b1 / BK, tB1 = (e1 + BK - 1) / BK;
+  if (e1 <= b1) tB1 = tB0;
+  if (tB0 < nA) tB0 = nA;
+  const int nB = tB1 > tB0 ? tB1 - tB0 : 0;
+  const int nt = nA + nB;
+
+  // ---- running statistics (raw-score units for the max)
+  constexpr float NEG_INF = -__builtin_inff();
+  float m_run = NEG_INF, l_run = 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+
+  u32x4 kreg[Cfg::NKL];
+  u32x4 vreg[4];
+
+  auto tile_of = [&](int t) { return t < nA ? t : tB0 + (t - nA); };
+
+  auto load_tile = [&](int jt) {
+    const int j0 = jt * BK;
+#pragma unroll
+    for (int it = 0; it < Cfg::NKL; ++it) {
+      const int c = tid + Cfg::NT * it;
+      const int row = c / CPR, col = c % CPR;
+      const int j = j0 + row;
+      kreg[it] = j < p.Sk ? *reinterpret_cast<const u32x4*>(kp + (long)j * p.rs + col * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < Cfg::NVU) {
+      const int dc = tid % CPR, kq = tid / CPR;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + 4 * kq + r;
+        vreg[r] = j < p.Sk ? *reinterpret_cast<const u32x4*>(vp + (long)j * p.rs + dc * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < Cfg::NKL; ++it) {
+      const int c = tid + Cfg::NT * it;
+      const int row = c / CPR, col = c % CPR;
+      *reinterpret_cast<u32x4*>(&Ks[buf][row * KP + col * 8]) = kreg[it];
+    }
+    if (tid < Cfg::NVU) {
+      const int dc = tid % CPR, kq = tid / CPR;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        const uint32_t a0 = (vreg[0][e >> 1] >> sh) & 0xffffu, a1 = (vreg[1][e >> 1] >> sh) & 0xffffu;
+        const uint32_t a2 = (vreg[2][e >> 1] >> sh) & 0xffffu, a3 = (vreg[3][e >> 1] >> sh) & 0xffffu;
+        u32x2 val;
+        val[0] = a0 | (a1 << 16);
+        val[1] = a2 | (a3 << 16);
+        *reinterpret_cast<u32x2*>(&Vt[buf][(8 * dc + e) * VP + 4 * kq]) = val;
+      }
+    }
+  };
+
+  if (nt > 0) load_tile(tile_of(0));
+
+  for (int t = 0; t < nt; ++t) {
+    const int buf = t & 1;
+    const int jt = tile_of(t);
+    const int j0 = jt * BK;
+    store_tile(buf);
+    __syncthreads();
+    if (t + 1 < nt) load_tile(tile_of(t + 1));
+
+    // wave-level tile class
+    int cls = kSkip;
+    if (wave_live) {
+      const int jend = min(j0 + BK, p.Sk);
+      int kmn, kmx;
+      seg_range(p.ks, j0, jend, kmn, kmx);
+      const bool tail = j0 + BK > p.Sk;
+      if (!p.causal) cls = tail ? kPartial : kFull;
+      else if (kmn > qmax_w) cls = kSkip;
+      else if (kmx <= qmin_w && !tail) cls = kFull;
+      else cls = kPartial;
+    }
+    if (cls == kSkip) continue;
+
+    // S^T = K Q^T for 64 keys (two 32-key blocks)
+    f32x16 st[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      st[mb] = f32x16{};
+      const uint16_t* krow = &Ks[buf][(mb * 32 + ln) * KP + 8 * g];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + ks * 16);
+        st[mb] = mfma32(as_bf16x8(a), qf[ks], st[mb]);
+      }
+    }
+
+    if (cls == kPartial) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool ok = j < p.Sk && (!p.causal || seg_pos(p.ks, j) <= qpos);
+          if (!ok) st[mb][r] = NEG_INF;
+        }
+      }
+    }
+
+    // online softmax: tile max, conditional rescale, exponentials, partial sums
+    float mx = NEG_INF;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m_run, mx);
+    if (__any(mnew > m_run)) {
+      const float alpha = (m_run == NEG_INF) ? 0.f : fast_exp2((m_run - mnew) * p.c);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      m_run = mnew;
+    }
+    const float msub = (m_run == NEG_INF) ? 0.f : m_run * p.c;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(__builtin_fmaf(st[mb][r], p.c, -msub));
+        st[mb][r] = e;
+        l_run += e;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int o = 8 * kk;
+        pb[2 * mb + kk] = pack_bf16x8(st[mb][o + 0], st[mb][o + 1], st[mb][o + 2], st[mb][o + 3], st[mb][o + 4],
+                                      st[mb][o + 5], st[mb][o + 6], st[mb][o + 7]);
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint16_t* vrow = &Vt[buf][(db * 32 + ln) * VP + 4 * g];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kb * 16);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kb * 16 + 8);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[db] = mfma32(as_bf16x8(a), pb[kb], oacc[db]);
+      }
+    }
+  }
+
+  // ---- epilogue: normalise, write O and LSE
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const bool has = lt > 0.f;
+  const float inv = has ? 1.f / lt : 0.f;
+  if (p.o_bf16) {
+    uint16_t* op = static_cast<uint16_t*>(p.o) + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * g;
+        u32x2 val;
+        val[0] = pack_bf16x2(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv);
+        val[1] = pack_bf16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + d0) = val;
+      }
+  } else {
+    float* op = static_cast<float*>(p.o) + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * g;
+        f32x4 val = {oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv, oacc[db][4 * q4 + 2] * inv,
+                     oacc[db][4 * q4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(op + d0) = val;
+      }
+  }
+  if (g == 0) {
+    const float lse = has ? (m_run * p.scale + logf(lt)) : NEG_INF;
+    p.lse[b * p.lse_bstride + (long)qrow * p.H + h] = lse;
+  }
+}
+
+static Seg to_seg(const SegArg& s) { return Seg{s.s0, s.l0, s.s1, s.n}; }
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  FwdParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.rs = (long)a.H * a.D;
+  p.q_bstride = (long)a.q_batch_rows * p.rs;
+  p.k_bstride = (long)a.k_batch_rows * p.rs;
+  p.lse_bstride = (long)a.q_batch_rows * a.H;
+  p.H = a.H;
+  p.Sq = a.Sq;
+  p.Sk = a.Sk;
+  p.qs = to_seg(a.qs);
+  p.ks = to_seg(a.ks);
+  p.causal = a.causal;
+  p.o_bf16 = a.o_bf16;
+  p.scale = a.scale;
+  p.c = a.scale * kLog2e;
+  const int BQ = 128;
+  p.nqb = (a.Sq + BQ - 1) / BQ;
+  const long nwg = (long)a.B * a.H * p.nqb;
+  if (nwg == 0) return hipSuccess;
+  dim3 grid((unsigned)nwg), block(256);
+  if (a.D == 64)
+    hipLaunchKernelGGL(fwd_kernel<64>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(fwd_kernel<128>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace ea

@@ -1,0 +1,113 @@
+"""Host-side drivers of the attention path on one GPU (no collectives).
+
+``ZigzagRingRank`` runs one rank's share of a zigzag ring attention layer:
+the ring visits every rank's key/value share in turn (EasyContext
+core-technology page, hotelren.com, section 1 "sequence parallelism"), with
+tokens interleaved across ranks (mlqm.cn training-script walkthrough, zigzag
+mode).  Here the W key/value shares sit side by side in one buffer, so the
+ring's send/receive is a pointer offset; every step is an ``ea_attn_fwd`` /
+``ea_attn_bwd`` call and the per-step partial results are combined with
+``ea_lse_merge``.  Positions come from ``ea_zigzag_segments``, and the causal
+rule on global positions selects, per step, the full, causal or half blocks.
+
+``DenseCausal`` is the whole-sequence case: one forward and one backward
+call over positions 0..S-1.
+
+All buffers are allocated when the driver is built; ``forward`` and
+``backward`` enqueue work on the current stream and allocate nothing.
+"""
+import torch
+
+from . import _lib as L
+
+
+class DenseCausal:
+    def __init__(self, q, k, v, causal=True, scale=None, o_dtype=torch.float32):
+        B, S, H, D = q.shape
+        self.q, self.k, self.v = q, k, v
+        self.causal = causal
+        self.scale = D ** -0.5 if scale is None else scale
+        dev = q.device
+        self.o = torch.empty((B, S, H, D), dtype=o_dtype, device=dev)
+        self.lse = torch.empty((B, S, H), dtype=torch.float32, device=dev)
+        self.delta = torch.empty((B, S, H), dtype=torch.float32, device=dev)
+        self.dq = torch.empty((B, S, H, D), dtype=torch.float32, device=dev)
+        self.dk = torch.empty((B, k.shape[1], H, D), dtype=torch.float32, device=dev)
+        self.dv = torch.empty_like(self.dk)
+        self.q_seg = [0, S]
+        self.k_seg = [0, k.shape[1]]
+
+    def forward(self, stream=None):
+        L.ea_attn_fwd(self.q, self.k, self.v, self.o, self.lse, self.q_seg, self.k_seg, self.causal, self.scale,
+                      stream)
+
+    def backward(self, do, stream=None):
+        self.dq.zero_()
+        self.dk.zero_()
+        self.dv.zero_()
+        L.ea_attn_bwd(self.q, self.k, self.v, self.o, do, self.lse, self.delta, self.dq, self.dk, self.dv,
+                      self.q_seg, self.k_seg, self.causal, self.scale, delta_ready=False, stream=stream)
+
+    def step(self, do, stream=None):
+        self.forward(stream)
+        self.backward(do, stream)
+
+
+class ZigzagRingRank:
+    """One rank of a W-rank zigzag ring.
+
+    q, do: [B, 2C, H, D] bf16, the rank's local rows (chunk r then chunk 2W-1-r).
+    k, v:  [B, W*2C, H, D] bf16, the W ranks' shares side by side: rows
+           [2C*s, 2C*(s+1)) are rank s's local keys/values.
+    """
+
+    def __init__(self, q, k, v, world, rank, scale=None):
+        B, sq, H, D = q.shape
+        if sq % 2 or k.shape[1] != world * sq:
+            raise ValueError("q must hold 2C rows and k/v W*2C rows")
+        self.q, self.k, self.v = q, k, v
+        self.W, self.r = world, rank
+        self.C = sq // 2
+        self.s_total = world * sq
+        self.scale = D ** -0.5 if scale is None else scale
+        dev = q.device
+        self.o = torch.empty((B, sq, H, D), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, sq, H), dtype=torch.float32, device=dev)
+        self.o_part = torch.empty_like(self.o)
+        self.lse_part = torch.empty_like(self.lse)
+        self.delta = torch.empty_like(self.lse)
+        self.dq = torch.empty_like(self.o)
+        self.dk = torch.empty((B, k.shape[1], H, D), dtype=torch.float32, device=dev)
+        self.dv = torch.empty_like(self.dk)
+        self.q_seg = L.ea_zigzag_segments(self.s_total, world, rank)
+        self.sources = [L.ea_ring_source(rank, t, world) for t in range(world)]
+        self.k_segs = [L.ea_zigzag_segments(self.s_total, world, s) for s in self.sources]
+
+    def _block(self, t, x):
+        s = self.sources[t]
+        return x[:, 2 * self.C * s: 2 * self.C * (s + 1)]
+
+    def forward(self, stream=None):
+        for t in range(self.W):
+            kb, vb = self._block(t, self.k), self._block(t, self.v)
+            if t == 0:
+                L.ea_attn_fwd(self.q, kb, vb, self.o, self.lse, self.q_seg, self.k_segs[t], True, self.scale,
+                              stream)
+            else:
+                L.ea_attn_fwd(self.q, kb, vb, self.o_part, self.lse_part, self.q_seg, self.k_segs[t], True,
+                              self.scale, stream)
+                L.ea_lse_merge(self.o, self.lse, self.o_part, self.lse_part, stream)
+
+    def backward(self, do, stream=None):
+        self.dq.zero_()
+        self.dk.zero_()
+        self.dv.zero_()
+        for t in range(self.W):
+            kb, vb = self._block(t, self.k), self._block(t, self.v)
+            L.ea_attn_bwd(self.q, kb, vb, self.o, do, self.lse, self.delta, self.dq, self._block(t, self.dk),
+                          self._block(t, self.dv), self.q_seg, self.k_segs[t], True, self.scale,
+                          delta_ready=(t > 0), stream=stream)
+
+    def step(self, do, stream=None):
+        self.forward(stream)
+        self.backward(do, stream)

@@ -1,0 +1,214 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small and mid sizes that span several tiles with ragged tails, both masks, two
+position segments, batch strides, bf16 and fp32 outputs, edge cases, and the
+zigzag ring of one rank; full-size workloads live in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import long_context_causal_ea_amd as ea
+import synth
+from tests.parity import assert_close, assert_lse, banner, scale_of, seg_positions, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _rand(shape, seed, std=1.0):
+    return synth.normal_draw(shape, seed, std, DEV).to(torch.bfloat16)
+
+
+def _sentinel(shape, dtype, pad=4096):
+    """Tensor view with NaN guard bands before and after (to catch stray writes)."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * pad,), float("nan"), dtype=dtype, device=DEV)
+    return buf, buf[pad:pad + n].view(shape), pad
+
+
+def _guards_intact(buf, pad):
+    return bool(torch.isnan(buf[:pad].float()).all()) and bool(torch.isnan(buf[-pad:].float()).all())
+
+
+def _run_dense(q, k, v, do, q_seg, k_seg, causal, o_dtype=torch.float32, scale=None):
+    B, sq, H, D = q.shape
+    sk = k.shape[1]
+    scale = scale_of(D) if scale is None else scale
+    ob, o, po = _sentinel((B, sq, H, D), o_dtype)
+    lb, lse, pl = _sentinel((B, sq, H), torch.float32)
+    ea.ea_attn_fwd(q, k, v, o, lse, q_seg, k_seg, causal, scale)
+    dqb, dq, p1 = _sentinel((B, sq, H, D), torch.float32)
+    dkb, dk, p2 = _sentinel((B, sk, H, D), torch.float32)
+    dvb, dv, p3 = _sentinel((B, sk, H, D), torch.float32)
+    dlb, delta, p4 = _sentinel((B, sq, H), torch.float32)
+    dq.zero_(), dk.zero_(), dv.zero_()
+    ea.ea_attn_bwd(q, k, v, o, do, lse, delta, dq, dk, dv, q_seg, k_seg, causal, scale)
+    torch.cuda.synchronize()
+    for buf, pad in ((ob, po), (lb, pl), (dqb, p1), (dkb, p2), (dvb, p3), (dlb, p4)):
+        assert _guards_intact(buf, pad), "write outside an output buffer"
+    return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
+
+
+def _check_dense(res, q, k, v, do, q_seg, k_seg, causal, scale=None, o_tol=None):
+    B, sq, H, D = q.shape
+    scale = scale_of(D) if scale is None else scale
+    pq, pk = seg_positions(q_seg), seg_positions(k_seg)
+    ref = oracle.attn_bwd_heads(q, k, v, do, pq, pk, causal, scale)
+    if res["o"].dtype == torch.bfloat16:
+        # a bf16 output carries its own rounding (2^-9 relative): gate its rel-L2 only
+        assert_close("O(bf16)", res["o"], ref["o"], max_abs=float("inf"))
+    else:
+        assert_close("O", res["o"], ref["o"])
+    assert_lse("LSE", res["lse"], ref["lse"])
+    assert_close("dQ", res["dq"], ref["dq"])
+    assert_close("dK", res["dk"], ref["dk"])
+    assert_close("dV", res["dv"], ref["dv"])
+    return ref
+
+
+def test_c1_all_heads():
+    cfg = synth.get("c1")
+    banner(f"{cfg.name}")
+    t = synth.make_dense_case(cfg, DEV)
+    res = _run_dense(t["q"], t["k"], t["v"], t["do"], [0, cfg.S], [0, cfg.S], True)
+    _check_dense(res, t["q"], t["k"], t["v"], t["do"], [0, cfg.S], [0, cfg.S], True)
+
+
+CASES = [
+    # D, B, Sq, Sk, causal, q_seg, k_seg, o_dtype
+    (128, 1, 200, 333, True, [133, 200], [0, 333], torch.float32),
+    (128, 1, 333, 200, False, [0, 333], [0, 200], torch.float32),
+    (64, 2, 257, 257, True, [0, 257], [0, 257], torch.float32),
+    (128, 1, 300, 700, True, [50, 150, 550, 150], [0, 350, 350, 350], torch.float32),  # two segments each
+    (128, 1, 128, 512, True, [0, 64, 448, 64], [0, 256, 256, 256], torch.bfloat16),
+    (64, 1, 1, 1, True, [7, 1], [3, 1], torch.float32),
+    (128, 1, 1, 450, True, [449, 1], [0, 450], torch.float32),
+    (128, 1, 450, 1, True, [0, 450], [0, 1], torch.float32),
+    (128, 1, 190, 190, True, [0, 190], [100, 190], torch.float32),  # rows 0..99 see no key
+    (64, 3, 70, 130, False, [0, 70], [0, 130], torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"case{i}" for i in range(len(CASES))])
+def test_dense_cases(case):
+    D, B, sq, sk, causal, q_seg, k_seg, o_dtype = case
+    banner(f"D={D} B={B} Sq={sq} Sk={sk} causal={causal} q_seg={q_seg} k_seg={k_seg} o={o_dtype}")
+    H = 3
+    q, k, v, do = (_rand((B, s, H, D), 50 + i) for i, s in enumerate((sq, sk, sk, sq)))
+    res = _run_dense(q, k, v, do, q_seg, k_seg, causal, o_dtype)
+    _check_dense(res, q, k, v, do, q_seg, k_seg, causal)
+
+
+def test_batch_row_stride_views():
+    """Row sub-ranges of larger buffers (pointer offsets, parent batch stride)."""
+    banner("views with batch_rows > S")
+    B, S, H, D = 2, 300, 2, 128
+    Q, K, V, DO = (_rand((B, S, H, D), 70 + i) for i in range(4))
+    q, do = Q[:, 100:260], DO[:, 100:260]
+    k, v = K[:, 40:290], V[:, 40:290]
+    q_seg, k_seg = [100, 160], [40, 250]
+    O = torch.zeros((B, S, H, D), device=DEV)
+    LSE = torch.zeros((B, S, H), device=DEV)
+    DQ = torch.zeros((B, S, H, D), device=DEV)
+    DK = torch.zeros_like(DQ)
+    DV = torch.zeros_like(DQ)
+    DL = torch.zeros_like(LSE)
+    ea.ea_attn_fwd(q, k, v, O[:, 100:260], LSE[:, 100:260], q_seg, k_seg, True)
+    ea.ea_attn_bwd(q, k, v, O[:, 100:260], do, LSE[:, 100:260], DL[:, 100:260], DQ[:, 100:260], DK[:, 40:290],
+                   DV[:, 40:290], q_seg, k_seg, True)
+    torch.cuda.synchronize()
+    assert float(O[:, :100].abs().max()) == 0 and float(O[:, 260:].abs().max()) == 0
+    assert float(DK[:, :40].abs().max()) == 0 and float(DK[:, 290:].abs().max()) == 0
+    ref = oracle.attn_bwd_heads(q, k, v, do, seg_positions(q_seg), seg_positions(k_seg), True, scale_of(D))
+    assert_close("O", O[:, 100:260], ref["o"])
+    assert_lse("LSE", LSE[:, 100:260], ref["lse"])
+    assert_close("dQ", DQ[:, 100:260], ref["dq"])
+    assert_close("dK", DK[:, 40:290], ref["dk"])
+    assert_close("dV", DV[:, 40:290], ref["dv"])
+
+
+def test_empty_keys():
+    banner("Sk = 0")
+    q = _rand((1, 130, 2, 64), 1)
+    k = torch.zeros((1, 0, 2, 64), dtype=torch.bfloat16, device=DEV)
+    o = torch.full((1, 130, 2, 64), 5.0, device=DEV)
+    lse = torch.zeros((1, 130, 2), device=DEV)
+    ea.ea_attn_fwd(q, k, k, o, lse, [0, 130], [0, 0], True)
+    dq = torch.full((1, 130, 2, 64), 2.0, device=DEV)
+    dl = torch.zeros((1, 130, 2), device=DEV)
+    ea.ea_attn_bwd(q, k, k, o, q, lse, dl, dq, k.float(), k.float(), [0, 130], [0, 0], True)
+    torch.cuda.synchronize()
+    assert float(o.abs().max()) == 0
+    assert bool(torch.isneginf(lse).all())
+    assert float((dq - 2.0).abs().max()) == 0
+
+
+def test_accumulation_adds():
+    """bwd adds into dq/dk/dv: two identical calls give twice one call."""
+    banner("accumulation")
+    B, S, H, D = 1, 200, 2, 128
+    q, k, v, do = (_rand((B, S, H, D), 90 + i) for i in range(4))
+    r1 = _run_dense(q, k, v, do, [0, S], [0, S], True)
+    dq, dk, dv = r1["dq"].clone(), r1["dk"].clone(), r1["dv"].clone()
+    ea.ea_attn_bwd(q, k, v, r1["o"], do, r1["lse"], r1["delta"], dq, dk, dv, [0, S], [0, S], True,
+                   delta_ready=True)
+    torch.cuda.synchronize()
+    for a, b in ((dq, r1["dq"]), (dk, r1["dk"]), (dv, r1["dv"])):
+        assert float((a - 2 * b).abs().max()) <= 1e-5 * max(1.0, float(b.abs().max()))
+
+
+def test_merge_against_oracle():
+    banner("lse merge")
+    B, S, H, D = 2, 300, 3, 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    oa = torch.randn((B, S, H, D), generator=g, device=DEV)
+    op = torch.randn((B, S, H, D), generator=g, device=DEV)
+    la = torch.randn((B, S, H), generator=g, device=DEV) * 3
+    lp = torch.randn((B, S, H), generator=g, device=DEV) * 3
+    la[0, :50] = float("-inf")
+    oa[0, :50] = 0
+    lp[0, 25:75] = float("-inf")
+    op[0, 25:75] = 0
+    ref_o, ref_l = oracle.lse_merge(oa.cpu(), la.cpu(), op.cpu(), lp.cpu())
+    ea.ea_lse_merge(oa, la, op, lp)
+    torch.cuda.synchronize()
+    assert_close("O", oa, ref_o, max_abs=1e-5, rel_l2=1e-6)
+    assert_lse("LSE", la, ref_l, tol=1e-5)
+    # bf16 partial
+    oa2 = torch.randn((1, 64, 2, 64), generator=g, device=DEV)
+    la2 = torch.randn((1, 64, 2), generator=g, device=DEV)
+    op2 = torch.randn((1, 64, 2, 64), generator=g, device=DEV).to(torch.bfloat16)
+    lp2 = torch.randn((1, 64, 2), generator=g, device=DEV)
+    ref_o2, ref_l2 = oracle.lse_merge(oa2.cpu(), la2.cpu(), op2.cpu(), lp2.cpu())
+    ea.ea_lse_merge(oa2, la2, op2, lp2)
+    torch.cuda.synchronize()
+    assert_close("O(bf16 part)", oa2, ref_o2, max_abs=1e-5, rel_l2=1e-6)
+    assert_lse("LSE(bf16 part)", la2, ref_l2, tol=1e-5)
+
+
+@pytest.mark.parametrize("rank", [0, 3, 7])
+@pytest.mark.parametrize("C,D", [(100, 128), (64, 64), (37, 128)])
+def test_zigzag_ring_small(rank, C, D):
+    W, H = 8, 2
+    banner(f"zigzag ring W={W} C={C} rank={rank} D={D}")
+    cfg = synth.get("c3")
+    t = synth.make_ring_case(cfg, DEV, C=C, H=H, rank=rank) if D == 128 else None
+    if t is None:
+        t = {n: _rand((1, s, H, D), 300 + i) for i, (n, s) in
+             enumerate((("q", 2 * C), ("k", 2 * W * C), ("v", 2 * W * C), ("do", 2 * C)))}
+    drv = ea.ZigzagRingRank(t["q"], t["k"], t["v"], W, rank)
+    drv.step(t["do"])
+    torch.cuda.synchronize()
+    S = 2 * W * C
+    pq = oracle.zigzag_positions(S, W, rank)
+    # K/V rows are the W ranks' shares side by side
+    pk = np.concatenate([oracle.zigzag_positions(S, W, s) for s in range(W)])
+    ref = oracle.attn_bwd_heads(t["q"], t["k"], t["v"], t["do"], pq, pk, True, scale_of(D))
+    assert_close("O", drv.o, ref["o"])
+    assert_lse("LSE", drv.lse, ref["lse"])
+    assert_close("dQ", drv.dq, ref["dq"])
+    assert_close("dK", drv.dk, ref["dk"])
+    assert_close("dV", drv.dv, ref["dv"])
