@@ -7,18 +7,32 @@
 //  2. dkdv:   one workgroup per 128-key block (4 waves x 32 keys).  Each wave
 //             keeps its keys' K and V rows in registers and its dK^T, dV^T
 //             accumulators in fp32 registers, and streams 32-row query tiles
-//             (Q, dO in both row-major and transposed form, LSE, Delta) through
-//             double-buffered LDS.  Scores are computed with the key on the
-//             MFMA column (lane) axis, so P and dS come out of the MFMA already
-//             in the B-operand form that dV^T += dO^T P and dK^T += Q^T dS need.
-//  3. dq:     one workgroup per 128-query block, streaming 64-key tiles like the
+//             (Q, dO, LSE, Delta) through double-buffered LDS.  Scores are
+//             computed with the key on the MFMA column (lane) axis, so P and dS
+//             come out of the MFMA already in the B-operand form that
+//             dV^T += dO^T P and dK^T += Q^T dS need; the dO^T and Q^T operands
+//             are read from the row-major tiles with the LDS transpose read.
+//  3. dq:     one workgroup per 128-query block, streaming key tiles like the
 //             forward; recomputes S^T and dP^T with the query on the lane axis
-//             and accumulates dQ^T += K^T dS^T in registers.
+//             and accumulates dQ^T += K^T dS^T in registers (K^T by transpose
+//             read of the row-major K tile).
+// All LDS tiles are row-major with the XOR chunk swizzle of ea_device.h.
 // The dq pass recomputes the two score products instead of exchanging dS
 // through atomics: every output element is then written by exactly one
 // workgroup, without atomics, and results are bitwise reproducible.
 #include "ea_device.h"
 #include "ea_launch.h"
+
+// Tile and occupancy choices (workgroups per CU the register budget is sized for).
+#ifndef EA_DQ_BK
+#define EA_DQ_BK 32
+#endif
+#ifndef EA_DQ_MIN_WG
+#define EA_DQ_MIN_WG 2
+#endif
+#ifndef EA_DKDV_MIN_WG
+#define EA_DKDV_MIN_WG 1
+#endif
 
 namespace ea {
 
@@ -85,22 +99,19 @@ __device__ __forceinline__ float lse_to_log2(float l) {
 template <int D>
 struct DkdvCfg {
   static constexpr int BKV = 128, BQ = 32, NT = 256;
-  static constexpr int KP = D + 8;     // row-major tile stride
-  static constexpr int TP = BQ + 8;    // transposed tile stride
   static constexpr int CPR = D / 8;
-  static constexpr int NU = (BQ / 4) * CPR;  // transposing units per tensor
-  static constexpr int LDS_R = BQ * KP, LDS_T = D * TP;
+  static constexpr int NQL = BQ * CPR / NT;  // 16-byte chunks per thread per tile (each of Q and dO)
+  static constexpr int LDS_T = BQ * D;
+  static_assert(NQL * NT == BQ * CPR, "unsupported query tile");
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, EA_DKDV_MIN_WG) void dkdv_kernel(BwdParams p) {
   using Cfg = DkdvCfg<D>;
-  constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, KP = Cfg::KP, TP = Cfg::TP, CPR = Cfg::CPR;
+  constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, CPR = Cfg::CPR;
   constexpr int NKS = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][Cfg::LDS_R];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[2][Cfg::LDS_R];   // dO, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][Cfg::LDS_T];
-  __shared__ __attribute__((aligned(16))) uint16_t Ot[2][Cfg::LDS_T];   // dO, transposed
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][Cfg::LDS_T];
+  __shared__ __attribute__((aligned(16))) uint16_t Os[2][Cfg::LDS_T];   // dO
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
 
@@ -137,6 +148,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     }
   }
   const int kpos = seg_pos(p.ks, key_ok ? krow : (p.Sk - 1));
+  QueryWindow qwin = query_window(p.qs, kpos, p.causal);
+  if (!key_ok) qwin = QueryWindow{0, 0, 0, 0};
 
   // key position ranges (workgroup and wave)
   const int wg_end = min(j0 + BKV, p.Sk);
@@ -177,23 +190,20 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     dva[db] = f32x16{};
   }
 
-  // staging: threads [0,128) carry Q units, [128,256) dO units; 4 rows x 8 dims each
-  const int half = tid >> 7, u = tid & 127;
-  const bool unit_ok = u < Cfg::NU;
-  const int udc = u % CPR, ukq = u / CPR;
-  const uint16_t* src_base = half ? op : qp;
-  u32x4 sreg[4];
+  // staging: consecutive threads take consecutive 16-byte chunks of a row
+  u32x4 qreg[Cfg::NQL], oreg[Cfg::NQL];
   float lreg = 0.f;
 
   auto load_tile = [&](int it) {
     const int i0 = it * BQ;
-    if (unit_ok) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * ukq + r;
-        sreg[r] = i < p.Sq ? *reinterpret_cast<const u32x4*>(src_base + (long)i * p.rs + udc * 8)
-                           : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int k = 0; k < Cfg::NQL; ++k) {
+      const int c = tid + Cfg::NT * k;
+      const int row = c / CPR, col = c % CPR;
+      const int i = i0 + row;
+      const long off = (long)i * p.rs + col * 8;
+      qreg[k] = i < p.Sq ? *reinterpret_cast<const u32x4*>(qp + off) : u32x4{0u, 0u, 0u, 0u};
+      oreg[k] = i < p.Sq ? *reinterpret_cast<const u32x4*>(op + off) : u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < 2 * BQ) {
       const int i = i0 + (tid % BQ);
@@ -204,27 +214,22 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     }
   };
   auto store_tile = [&](int buf) {
-    if (unit_ok) {
-      uint16_t* rm = half ? Os[buf] : Qs[buf];
-      uint16_t* tr = half ? Ot[buf] : Qt[buf];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4*>(&rm[(4 * ukq + r) * KP + udc * 8]) = sreg[r];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        const uint32_t x0 = (sreg[0][e >> 1] >> sh) & 0xffffu, x1 = (sreg[1][e >> 1] >> sh) & 0xffffu;
-        const uint32_t x2 = (sreg[2][e >> 1] >> sh) & 0xffffu, x3 = (sreg[3][e >> 1] >> sh) & 0xffffu;
-        u32x2 val;
-        val[0] = x0 | (x1 << 16);
-        val[1] = x2 | (x3 << 16);
-        *reinterpret_cast<u32x2*>(&tr[(8 * udc + e) * TP + 4 * ukq]) = val;
-      }
+    for (int k = 0; k < Cfg::NQL; ++k) {
+      const int c = tid + Cfg::NT * k;
+      const int o = tile_off<D>(c / CPR, c % CPR);
+      *reinterpret_cast<u32x4*>(&Qs[buf][o]) = qreg[k];
+      *reinterpret_cast<u32x4*>(&Os[buf][o]) = oreg[k];
     }
     if (tid < BQ)
       Ls[buf][tid] = lreg;
     else if (tid < 2 * BQ)
       Ds[buf][tid - BQ] = lreg;
   };
+
+  const int swq = swz<D>(ln);                                  // Q/dO operand rows are ln
+  const int trow = 4 * g + ((lane & 15) >> 2);                 // transpose read: row within a 16-query step
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // transpose read: column within 32 dims
 
   if (nt > 0) load_tile(tile_of(0));
 
@@ -252,16 +257,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     // S = Q K^T and dP = dO V^T; lane = key, register r = query 8(r/4)+4g+r%4
     f32x16 s = f32x16{}, dp = f32x16{};
     {
-      const uint16_t* qrow = &Qs[buf][ln * KP + 8 * g];
-      const uint16_t* orow = &Os[buf][ln * KP + 8 * g];
+      const uint16_t* qrow = &Qs[buf][ln * D];
+      const uint16_t* orow = &Os[buf][ln * D];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 aq = *reinterpret_cast<const u32x4*>(qrow + ks * 16);
+        const int o = ((2 * ks + g) ^ swq) << 3;
+        const u32x4 aq = *reinterpret_cast<const u32x4*>(qrow + o);
         s = mfma32(as_bf16x8(aq), kf[ks], s);
-      }
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 ao = *reinterpret_cast<const u32x4*>(orow + ks * 16);
+        const u32x4 ao = *reinterpret_cast<const u32x4*>(orow + o);
         dp = mfma32(as_bf16x8(ao), vf[ks], dp);
       }
     }
@@ -276,11 +279,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * q4 + e;
         float pv = fast_exp2(__builtin_fmaf(s[r], p.c, -l4[e]));
-        if (cls == kPartial) {
-          const int i = i0 + qi + e;
-          const bool ok = key_ok && i < p.Sq && (!p.causal || kpos <= seg_pos(p.qs, i));
-          if (!ok) pv = 0.f;
-        }
+        if (cls == kPartial) pv = in_window(qwin, i0 + qi + e) ? pv : 0.f;
         s[r] = pv;
         ds[r] = pv * (dp[r] - d4[e]);
       }
@@ -293,19 +292,21 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       sb[kk] = pack_bf16x8(ds[o], ds[o + 1], ds[o + 2], ds[o + 3], ds[o + 4], ds[o + 5], ds[o + 6], ds[o + 7]);
     }
 
-    // dV^T += dO^T P ; dK^T += Q^T dS   (reduction over the tile's 32 queries)
+    // dV^T += dO^T P ; dK^T += Q^T dS   (reduction over the tile's 32 queries;
+    // dO^T and Q^T read transposed from the row-major tiles)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint16_t* orow = &Ot[buf][(db * 32 + ln) * TP + 4 * g];
-      const uint16_t* qrow = &Qt[buf][(db * 32 + ln) * TP + 4 * g];
+      const int col = db * 32 + tcol;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const u32x2 olo = *reinterpret_cast<const u32x2*>(orow + 16 * kk);
-        const u32x2 ohi = *reinterpret_cast<const u32x2*>(orow + 16 * kk + 8);
+        const int o0 = tile_off<D>(kk * 16 + trow, col >> 3) + (col & 7);
+        const int o1 = tile_off<D>(kk * 16 + 8 + trow, col >> 3) + (col & 7);
+        const u32x2 olo = ds_read_tr16(&Os[buf][o0]);
+        const u32x2 ohi = ds_read_tr16(&Os[buf][o1]);
         const u32x4 ao = {olo[0], olo[1], ohi[0], ohi[1]};
         dva[db] = mfma32(as_bf16x8(ao), pb[kk], dva[db]);
-        const u32x2 qlo = *reinterpret_cast<const u32x2*>(qrow + 16 * kk);
-        const u32x2 qhi = *reinterpret_cast<const u32x2*>(qrow + 16 * kk + 8);
+        const u32x2 qlo = ds_read_tr16(&Qs[buf][o0]);
+        const u32x2 qhi = ds_read_tr16(&Qs[buf][o1]);
         const u32x4 aq = {qlo[0], qlo[1], qhi[0], qhi[1]};
         dka[db] = mfma32(as_bf16x8(aq), sb[kk], dka[db]);
       }
@@ -335,23 +336,21 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 // ------------------------------------------------------------------ dQ
 template <int D>
 struct DqCfg {
-  static constexpr int BQ = 128, BK = 64, NT = 256;
-  static constexpr int KP = D + 8;
-  static constexpr int TP = BK + 8;
+  static constexpr int BQ = 128, BK = EA_DQ_BK, NT = 256;
+  static constexpr int NMB = BK / 32, NKB = BK / 16;
   static constexpr int CPR = D / 8;
-  static constexpr int NKU = (BK / 4) * CPR;  // K transposing units
-  static constexpr int NVL = BK * CPR / NT;   // V chunks per thread
-  static constexpr int LDS_R = BK * KP, LDS_T = D * TP;
+  static constexpr int NKL = BK * CPR / NT;  // 16-byte chunks per thread per tile (each of K and V)
+  static constexpr int LDS_T = BK * D;
+  static_assert(BK % 32 == 0 && NKL * NT == BK * CPR, "unsupported key tile");
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, EA_DQ_MIN_WG) void dq_kernel(BwdParams p) {
   using Cfg = DqCfg<D>;
-  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, KP = Cfg::KP, TP = Cfg::TP, CPR = Cfg::CPR;
-  constexpr int NKS = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][Cfg::LDS_R];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][Cfg::LDS_R];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][Cfg::LDS_T];
+  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, CPR = Cfg::CPR;
+  constexpr int NKS = D / 16, NDB = D / 32, NMB = Cfg::NMB, NKB = Cfg::NKB;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][Cfg::LDS_T];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][Cfg::LDS_T];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ln = lane & 31, g = lane >> 5;
@@ -386,6 +385,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p) {
   const float lse2 = row_ok ? lse_to_log2(p.lse[srow]) : __builtin_inff();
   const float dlt = row_ok ? p.delta[srow] : 0.f;
   const int qpos = seg_pos(p.qs, row_ok ? qrow : (p.Sq - 1));
+  const KeyWindow kwin = key_window(p.ks, qpos, p.causal);
 
   const int wg_end = min(i0 + BQ, p.Sq);
   int qmin_wg, qmax_wg;
@@ -409,51 +409,34 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqa[db] = f32x16{};
 
-  // staging: K as 4-row units (row-major + transposed copies), V as 16-byte chunks
-  const bool kunit_ok = tid < Cfg::NKU;
-  const int udc = tid % CPR, ukq = tid / CPR;
-  u32x4 kreg[4];
-  u32x4 vreg[Cfg::NVL];
+  // staging: consecutive threads take consecutive 16-byte chunks of a row
+  u32x4 kreg[Cfg::NKL], vreg[Cfg::NKL];
 
   auto load_tile = [&](int jt) {
     const int j0 = jt * BK;
-    if (kunit_ok) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + 4 * ukq + r;
-        kreg[r] = j < p.Sk ? *reinterpret_cast<const u32x4*>(kp + (long)j * p.rs + udc * 8) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < Cfg::NVL; ++it) {
+    for (int it = 0; it < Cfg::NKL; ++it) {
       const int c = tid + Cfg::NT * it;
       const int row = c / CPR, col = c % CPR;
       const int j = j0 + row;
-      vreg[it] = j < p.Sk ? *reinterpret_cast<const u32x4*>(vp + (long)j * p.rs + col * 8) : u32x4{0u, 0u, 0u, 0u};
+      const long off = (long)j * p.rs + col * 8;
+      kreg[it] = j < p.Sk ? *reinterpret_cast<const u32x4*>(kp + off) : u32x4{0u, 0u, 0u, 0u};
+      vreg[it] = j < p.Sk ? *reinterpret_cast<const u32x4*>(vp + off) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto store_tile = [&](int buf) {
-    if (kunit_ok) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4*>(&Ks[buf][(4 * ukq + r) * KP + udc * 8]) = kreg[r];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        const uint32_t x0 = (kreg[0][e >> 1] >> sh) & 0xffffu, x1 = (kreg[1][e >> 1] >> sh) & 0xffffu;
-        const uint32_t x2 = (kreg[2][e >> 1] >> sh) & 0xffffu, x3 = (kreg[3][e >> 1] >> sh) & 0xffffu;
-        u32x2 val;
-        val[0] = x0 | (x1 << 16);
-        val[1] = x2 | (x3 << 16);
-        *reinterpret_cast<u32x2*>(&Kt[buf][(8 * udc + e) * TP + 4 * ukq]) = val;
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < Cfg::NVL; ++it) {
+    for (int it = 0; it < Cfg::NKL; ++it) {
       const int c = tid + Cfg::NT * it;
-      const int row = c / CPR, col = c % CPR;
-      *reinterpret_cast<u32x4*>(&Vs[buf][row * KP + col * 8]) = vreg[it];
+      const int o = tile_off<D>(c / CPR, c % CPR);
+      *reinterpret_cast<u32x4*>(&Ks[buf][o]) = kreg[it];
+      *reinterpret_cast<u32x4*>(&Vs[buf][o]) = vreg[it];
     }
   };
+
+  const int swk = swz<D>(ln);                                  // K/V operand rows are mb*32 + ln
+  const int trow = 4 * g + ((lane & 15) >> 2);                 // transpose read: row within a 16-key step
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // transpose read: column within 32 dims
 
   if (nt > 0) load_tile(tile_of(0));
 
@@ -478,36 +461,30 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p) {
     }
     if (cls == kSkip) continue;
 
-    f32x16 st[2], dpt[2];
+    f32x16 st[NMB], dpt[NMB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
       st[mb] = f32x16{};
       dpt[mb] = f32x16{};
-      const uint16_t* krow = &Ks[buf][(mb * 32 + ln) * KP + 8 * g];
-      const uint16_t* vrow = &Vs[buf][(mb * 32 + ln) * KP + 8 * g];
+      const uint16_t* krow = &Ks[buf][(mb * 32 + ln) * D];
+      const uint16_t* vrow = &Vs[buf][(mb * 32 + ln) * D];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + ks * 16);
+        const int o = ((2 * ks + g) ^ swk) << 3;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + o);
         st[mb] = mfma32(as_bf16x8(a), qf[ks], st[mb]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(vrow + ks * 16);
-        dpt[mb] = mfma32(as_bf16x8(a), of[ks], dpt[mb]);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(vrow + o);
+        dpt[mb] = mfma32(as_bf16x8(b), of[ks], dpt[mb]);
       }
     }
 
-    bf16x8 sb[4];
+    bf16x8 sb[NKB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = fast_exp2(__builtin_fmaf(st[mb][r], p.c, -lse2));
-        if (cls == kPartial) {
-          const int j = j0 + mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = j < p.Sk && (!p.causal || seg_pos(p.ks, j) <= qpos);
-          if (!ok) pv = 0.f;
-        }
+        if (cls == kPartial) pv = in_window(kwin, j0 + mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) ? pv : 0.f;
         st[mb][r] = pv * (dpt[mb][r] - dlt);
       }
 #pragma unroll
@@ -518,14 +495,14 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p) {
       }
     }
 
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T; K^T read transposed from the row-major K tile
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint16_t* krow = &Kt[buf][(db * 32 + ln) * TP + 4 * g];
+      const int col = db * 32 + tcol;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(krow + kb * 16);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(krow + kb * 16 + 8);
+      for (int kb = 0; kb < NKB; ++kb) {
+        const u32x2 lo = ds_read_tr16(&Ks[buf][tile_off<D>(kb * 16 + trow, col >> 3) + (col & 7)]);
+        const u32x2 hi = ds_read_tr16(&Ks[buf][tile_off<D>(kb * 16 + 8 + trow, col >> 3) + (col & 7)]);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         dqa[db] = mfma32(as_bf16x8(a), sb[kb], dqa[db]);
       }

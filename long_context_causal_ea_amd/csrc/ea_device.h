@@ -45,6 +45,37 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float x0, float x1, float x2, floa
   return as_bf16x8(u);
 }
 
+// ---- LDS tiles: row-major [rows][D] bf16, 16-byte chunks XOR-swizzled per row.
+// Chunk c of row r is stored at chunk slot c ^ swz(r).  The swizzle keeps both
+// access patterns of the kernels free of bank conflicts on 64 banks x 4 bytes:
+// (a) 16 lanes reading the same chunk of 16 consecutive rows (MFMA operands
+// whose reduction index runs along D), and (b) the transpose reads below, where
+// 32 lanes read 4 consecutive rows x 64 bytes.
+template <int D>
+__device__ __forceinline__ int swz(int r);
+template <>
+__device__ __forceinline__ int swz<128>(int r) {  // 16 chunks per row
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+template <>
+__device__ __forceinline__ int swz<64>(int r) {  // 8 chunks per row, two rows per 256 bytes
+  return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int chunk) {
+  return r * D + ((chunk ^ swz<D>(r)) << 3);
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, if lane i addresses the 4 elements T[r0 + i/4][c0 + 4*(i%4) .. +3] of a
+// row-major tile, lane j receives T[r0 + e][c0 + j] for e = 0..3: a 4 x 16 block
+// read transposed, i.e. 4 consecutive rows of one column per lane.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
+  short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // Exponent base 2 on the hardware transcendental unit.
@@ -86,6 +117,44 @@ __device__ __forceinline__ void causal_key_ranges(const Seg& k, int qmax, int& e
   n1 = n1 < 0 ? 0 : (n1 > len1 ? len1 : n1);
   b1 = k.l0;
   e1 = k.l0 + (int)n1;
+}
+
+// Key rows a query at position qpos may see, as [0, lim0) U [l0, lim1) of the
+// key tensor (under the full mask: [0, n)).  Computed once per query row, so
+// that the element mask of a partial tile is a few integer compares.
+struct KeyWindow {
+  int lim0, l0, lim1;
+};
+
+__device__ __forceinline__ KeyWindow key_window(const Seg& k, int qpos, bool causal) {
+  if (!causal) return KeyWindow{k.n, k.n, k.n};
+  long a = (long)qpos - k.s0 + 1;
+  a = a < 0 ? 0 : (a > k.l0 ? k.l0 : a);
+  long c = (long)k.l0 + ((long)qpos - k.s1 + 1);
+  c = c < k.l0 ? k.l0 : (c > k.n ? k.n : c);
+  return KeyWindow{(int)a, k.l0, (int)c};
+}
+
+__device__ __forceinline__ bool in_window(const KeyWindow& w, int j) {
+  return (j < w.lim0) | ((j >= w.l0) & (j < w.lim1));
+}
+
+// Query rows that may see a key at position kpos, as [lo0, hi0) U [lo1, n).
+struct QueryWindow {
+  int lo0, hi0, lo1, n;
+};
+
+__device__ __forceinline__ QueryWindow query_window(const Seg& q, int kpos, bool causal) {
+  if (!causal) return QueryWindow{0, q.n, q.n, q.n};
+  long a = (long)kpos - q.s0;
+  a = a < 0 ? 0 : (a > q.l0 ? q.l0 : a);
+  long c = (long)q.l0 + ((long)kpos - q.s1);
+  c = c < q.l0 ? q.l0 : (c > q.n ? q.n : c);
+  return QueryWindow{(int)a, q.l0, (int)c, q.n};
+}
+
+__device__ __forceinline__ bool in_window(const QueryWindow& w, int i) {
+  return ((i >= w.lo0) & (i < w.hi0)) | ((i >= w.lo1) & (i < w.n));
 }
 
 enum TileClass { kSkip = 0, kFull = 1, kPartial = 2 };

@@ -11,8 +11,9 @@
 //    every lane then holds 32 scores of ONE query row, so the row max and row
 //    sum are in-lane reductions plus one exchange with lane l^32.
 //  - P^T (bf16, round-to-nearest-even) feeds O^T += V^T P^T directly from
-//    registers; V is stored transposed in LDS so that the MFMA's reduction
-//    index (keys) is contiguous for each lane.
+//    registers.  K and V tiles are stored row-major in LDS with an XOR swizzle
+//    of 16-byte chunks; the V^T operand is read with the gfx950 LDS transpose
+//    read, so no transposed copy is ever written.
 //  - exp is computed as exp2 with scale*log2(e) folded into one FMA.
 //  - Tiles are classified per wave from global positions: SKIP (no allowed
 //    pair), FULL (all allowed, no mask work) or PARTIAL (element mask; also
@@ -37,24 +38,30 @@ struct FwdParams {
   float scale, c;  // c = scale * log2(e)
 };
 
+#ifndef EA_FWD_BK
+#define EA_FWD_BK 64
+#endif
+#ifndef EA_FWD_MIN_WG
+#define EA_FWD_MIN_WG 2  // workgroups per CU the register budget is sized for
+#endif
+
 template <int D>
 struct FwdCfg {
-  static constexpr int BQ = 128, BK = 64, NT = 256;
-  static constexpr int KP = D + 8;   // Ks row stride (elements): 16-byte skew per row
-  static constexpr int VP = BK + 8;  // Vt row stride
+  static constexpr int BQ = 128, BK = EA_FWD_BK, NT = 256;
+  static constexpr int NMB = BK / 32, NKB = BK / 16;  // 32-key MFMA blocks, 16-key reduction steps
   static constexpr int CPR = D / 8;  // 16-byte chunks per row
-  static constexpr int NKL = BK * CPR / NT;
-  static constexpr int NVU = (BK / 4) * CPR;  // transposing units (4 keys x 8 dims)
-  static constexpr int LDS_K = BK * KP, LDS_V = D * VP;
+  static constexpr int NKL = BK * CPR / NT;  // chunks per thread per tile (each of K and V)
+  static constexpr int LDS_T = BK * D;
+  static_assert(BK % 32 == 0 && NKL * NT == BK * CPR, "unsupported key tile");
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, EA_FWD_MIN_WG) void fwd_kernel(FwdParams p) {
   using Cfg = FwdCfg<D>;
-  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, KP = Cfg::KP, VP = Cfg::VP, CPR = Cfg::CPR;
-  constexpr int NKS = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][Cfg::LDS_K];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][Cfg::LDS_V];
+  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, CPR = Cfg::CPR;
+  constexpr int NKS = D / 16, NDB = D / 32, NMB = Cfg::NMB, NKB = Cfg::NKB;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][Cfg::LDS_T];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][Cfg::LDS_T];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ln = lane & 31, g = lane >> 5;
@@ -85,6 +92,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
     }
   }
   const int qpos = seg_pos(p.qs, row_ok ? qrow : (p.Sq - 1));
+  const KeyWindow kwin = key_window(p.ks, qpos, p.causal);
 
   // ---- position ranges of the workgroup's and this wave's valid rows
   const int wg_end = min(i0 + BQ, p.Sq);
@@ -112,11 +120,11 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
 
-  u32x4 kreg[Cfg::NKL];
-  u32x4 vreg[4];
+  u32x4 kreg[Cfg::NKL], vreg[Cfg::NKL];
 
   auto tile_of = [&](int t) { return t < nA ? t : tB0 + (t - nA); };
 
+  // global -> registers: consecutive threads take consecutive 16-byte chunks of a row
   auto load_tile = [&](int jt) {
     const int j0 = jt * BK;
 #pragma unroll
@@ -124,39 +132,28 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       const int c = tid + Cfg::NT * it;
       const int row = c / CPR, col = c % CPR;
       const int j = j0 + row;
-      kreg[it] = j < p.Sk ? *reinterpret_cast<const u32x4*>(kp + (long)j * p.rs + col * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < Cfg::NVU) {
-      const int dc = tid % CPR, kq = tid / CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + 4 * kq + r;
-        vreg[r] = j < p.Sk ? *reinterpret_cast<const u32x4*>(vp + (long)j * p.rs + dc * 8) : u32x4{0u, 0u, 0u, 0u};
-      }
+      const long off = (long)j * p.rs + col * 8;
+      kreg[it] = j < p.Sk ? *reinterpret_cast<const u32x4*>(kp + off) : u32x4{0u, 0u, 0u, 0u};
+      vreg[it] = j < p.Sk ? *reinterpret_cast<const u32x4*>(vp + off) : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
+  // registers -> LDS, swizzled row-major
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < Cfg::NKL; ++it) {
       const int c = tid + Cfg::NT * it;
       const int row = c / CPR, col = c % CPR;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * KP + col * 8]) = kreg[it];
-    }
-    if (tid < Cfg::NVU) {
-      const int dc = tid % CPR, kq = tid / CPR;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        const uint32_t a0 = (vreg[0][e >> 1] >> sh) & 0xffffu, a1 = (vreg[1][e >> 1] >> sh) & 0xffffu;
-        const uint32_t a2 = (vreg[2][e >> 1] >> sh) & 0xffffu, a3 = (vreg[3][e >> 1] >> sh) & 0xffffu;
-        u32x2 val;
-        val[0] = a0 | (a1 << 16);
-        val[1] = a2 | (a3 << 16);
-        *reinterpret_cast<u32x2*>(&Vt[buf][(8 * dc + e) * VP + 4 * kq]) = val;
-      }
+      const int o = tile_off<D>(row, col);
+      *reinterpret_cast<u32x4*>(&Ks[buf][o]) = kreg[it];
+      *reinterpret_cast<u32x4*>(&Vs[buf][o]) = vreg[it];
     }
   };
+
+  // per-lane pieces of the LDS addresses
+  const int swk = swz<D>(ln);                                  // K operand rows are mb*32 + ln
+  const int trow = 4 * g + ((lane & 15) >> 2);                 // transpose read: row within a 16-key step
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // transpose read: column within 32 dims
 
   if (nt > 0) load_tile(tile_of(0));
 
@@ -182,27 +179,26 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
     }
     if (cls == kSkip) continue;
 
-    // S^T = K Q^T for 64 keys (two 32-key blocks)
-    f32x16 st[2];
+    // S^T = K Q^T, one 32-key MFMA block at a time
+    f32x16 st[NMB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
       st[mb] = f32x16{};
-      const uint16_t* krow = &Ks[buf][(mb * 32 + ln) * KP + 8 * g];
+      const uint16_t* krow = &Ks[buf][(mb * 32 + ln) * D];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + ks * 16);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + (((2 * ks + g) ^ swk) << 3));
         st[mb] = mfma32(as_bf16x8(a), qf[ks], st[mb]);
       }
     }
 
     if (cls == kPartial) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = j0 + mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = j < p.Sk && (!p.causal || seg_pos(p.ks, j) <= qpos);
-          if (!ok) st[mb][r] = NEG_INF;
+          st[mb][r] = in_window(kwin, j) ? st[mb][r] : NEG_INF;
         }
       }
     }
@@ -210,7 +206,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
     // online softmax: tile max, conditional rescale, exponentials, partial sums
     float mx = NEG_INF;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -223,9 +219,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       m_run = mnew;
     }
     const float msub = (m_run == NEG_INF) ? 0.f : m_run * p.c;
-    bf16x8 pb[4];
+    bf16x8 pb[NKB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = fast_exp2(__builtin_fmaf(st[mb][r], p.c, -msub));
@@ -240,14 +236,15 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       }
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T; V^T read transposed from the row-major V tile
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint16_t* vrow = &Vt[buf][(db * 32 + ln) * VP + 4 * g];
+      const int col = db * 32 + tcol;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kb * 16);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kb * 16 + 8);
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int r0 = kb * 16 + trow, r1 = r0 + 8;
+        const u32x2 lo = ds_read_tr16(&Vs[buf][tile_off<D>(r0, col >> 3) + (col & 7)]);
+        const u32x2 hi = ds_read_tr16(&Vs[buf][tile_off<D>(r1, col >> 3) + (col & 7)]);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         oacc[db] = mfma32(as_bf16x8(a), pb[kb], oacc[db]);
       }
@@ -311,7 +308,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.o_bf16 = a.o_bf16;
   p.scale = a.scale;
   p.c = a.scale * kLog2e;
-  const int BQ = 128;
+  const int BQ = FwdCfg<128>::BQ;
   p.nqb = (a.Sq + BQ - 1) / BQ;
   const long nwg = (long)a.B * a.H * p.nqb;
   if (nwg == 0) return hipSuccess;
