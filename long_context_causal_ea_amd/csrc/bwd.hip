@@ -30,8 +30,8 @@
 #ifndef EA_DQ_MIN_WG
 #define EA_DQ_MIN_WG 2
 #endif
-#ifndef EA_DKDV_MIN_WG
-#define EA_DKDV_MIN_WG 1
+#ifndef EA_DKDV_WAVES
+#define EA_DKDV_WAVES 8  // waves per dK/dV workgroup (16 keys each); 4 or 8
 #endif
 
 namespace ea {
@@ -96,27 +96,32 @@ __device__ __forceinline__ float lse_to_log2(float l) {
 }
 
 // ------------------------------------------------------------------ dK, dV
+// One workgroup per block of NW*16 keys; each wave owns 16 keys.  The 16x16x32
+// MFMA puts the wave's 16 keys on the lane axis, so P and dS leave the score
+// products as B operands of dV^T += dO^T P and dK^T += Q^T dS, and the dK^T /
+// dV^T accumulators of 16 keys x D dims take D/2 registers each: two waves fit
+// per SIMD.
 template <int D>
 struct DkdvCfg {
-  static constexpr int BKV = 128, BQ = 32, NT = 256;
+  static constexpr int NW = EA_DKDV_WAVES, NT = 64 * NW, BKV = 16 * NW, BQ = 32;
   static constexpr int CPR = D / 8;
-  static constexpr int NQL = BQ * CPR / NT;  // 16-byte chunks per thread per tile (each of Q and dO)
+  static constexpr int NL = 2 * BQ * CPR / NT;  // 16-byte chunks per thread per tile (Q and dO together)
   static constexpr int LDS_T = BQ * D;
-  static_assert(NQL * NT == BQ * CPR, "unsupported query tile");
+  static_assert(NL * NT == 2 * BQ * CPR && NL >= 1, "unsupported query tile");
 };
 
 template <int D>
-__global__ __launch_bounds__(256, EA_DKDV_MIN_WG) void dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * EA_DKDV_WAVES, 8 / EA_DKDV_WAVES) void dkdv_kernel(BwdParams p) {
   using Cfg = DkdvCfg<D>;
-  constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, CPR = Cfg::CPR;
-  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, CPR = Cfg::CPR, NT = Cfg::NT;
+  constexpr int NKS = D / 32, NDB = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][Cfg::LDS_T];
   __shared__ __attribute__((aligned(16))) uint16_t Os[2][Cfg::LDS_T];   // dO
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int ln = lane & 31, g = lane >> 5;
+  const int l16 = lane & 15, g4 = lane >> 4;
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = work / p.nblk;
@@ -132,19 +137,20 @@ __global__ __launch_bounds__(256, EA_DKDV_MIN_WG) void dkdv_kernel(BwdParams p) 
   const float* delp = p.delta + b * p.row_bstride + h;
 
   const int j0 = kb * BKV;
-  const int kw0 = j0 + 32 * w;
-  const int krow = kw0 + ln;
+  const int kw0 = j0 + 16 * w;
+  const int krow = kw0 + l16;
   const bool key_ok = krow < p.Sk;
 
+  // this lane's key row in MFMA B-operand form (8 dims per lane per 32-dim step)
   bf16x8 kf[NKS], vf[NKS];
   {
-    const long off = (long)(key_ok ? krow : 0) * p.rs + 8 * g;
+    const long off = (long)(key_ok ? krow : 0) * p.rs + 8 * g4;
     const u32x4* ksrc = reinterpret_cast<const u32x4*>(kp + off);
     const u32x4* vsrc = reinterpret_cast<const u32x4*>(vp + off);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = as_bf16x8(key_ok ? ksrc[2 * ks] : u32x4{0u, 0u, 0u, 0u});
-      vf[ks] = as_bf16x8(key_ok ? vsrc[2 * ks] : u32x4{0u, 0u, 0u, 0u});
+      kf[ks] = as_bf16x8(key_ok ? ksrc[4 * ks] : u32x4{0u, 0u, 0u, 0u});
+      vf[ks] = as_bf16x8(key_ok ? vsrc[4 * ks] : u32x4{0u, 0u, 0u, 0u});
     }
   }
   const int kpos = seg_pos(p.ks, key_ok ? krow : (p.Sk - 1));
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(256, EA_DKDV_MIN_WG) void dkdv_kernel(BwdParams p) 
   const int wg_end = min(j0 + BKV, p.Sk);
   int kmin_wg, kmax_wg;
   seg_range(p.ks, j0, wg_end, kmin_wg, kmax_wg);
-  const int kw1 = min(kw0 + 32, p.Sk);
+  const int kw1 = min(kw0 + 16, p.Sk);
   const bool wave_live = kw0 < kw1;
   int kmin_w = 0x7fffffff, kmax_w = 0;
   if (wave_live) seg_range(p.ks, kw0, kw1, kmin_w, kmax_w);
@@ -183,27 +189,28 @@ __global__ __launch_bounds__(256, EA_DKDV_MIN_WG) void dkdv_kernel(BwdParams p) 
   const int nt = nA + nC;
   auto tile_of = [&](int t) { return t < nA ? tA0 + t : tC0 + (t - nA); };
 
-  f32x16 dka[NDB], dva[NDB];
+  f32x4 dka[NDB], dva[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    dka[db] = f32x16{};
-    dva[db] = f32x16{};
+    dka[db] = f32x4{};
+    dva[db] = f32x4{};
   }
 
-  // staging: consecutive threads take consecutive 16-byte chunks of a row
-  u32x4 qreg[Cfg::NQL], oreg[Cfg::NQL];
+  // staging: chunk c of the tile pair (Q rows then dO rows); consecutive threads
+  // take consecutive 16-byte chunks of a row
+  u32x4 sreg[Cfg::NL];
   float lreg = 0.f;
 
   auto load_tile = [&](int it) {
     const int i0 = it * BQ;
 #pragma unroll
-    for (int k = 0; k < Cfg::NQL; ++k) {
-      const int c = tid + Cfg::NT * k;
-      const int row = c / CPR, col = c % CPR;
+    for (int k = 0; k < Cfg::NL; ++k) {
+      const int c = tid + NT * k;
+      const int tns = c / (BQ * CPR), within = c % (BQ * CPR);
+      const int row = within / CPR, col = within % CPR;
       const int i = i0 + row;
-      const long off = (long)i * p.rs + col * 8;
-      qreg[k] = i < p.Sq ? *reinterpret_cast<const u32x4*>(qp + off) : u32x4{0u, 0u, 0u, 0u};
-      oreg[k] = i < p.Sq ? *reinterpret_cast<const u32x4*>(op + off) : u32x4{0u, 0u, 0u, 0u};
+      const uint16_t* src = tns ? op : qp;
+      sreg[k] = i < p.Sq ? *reinterpret_cast<const u32x4*>(src + (long)i * p.rs + col * 8) : u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < 2 * BQ) {
       const int i = i0 + (tid % BQ);
@@ -215,11 +222,11 @@ __global__ __launch_bounds__(256, EA_DKDV_MIN_WG) void dkdv_kernel(BwdParams p) 
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int k = 0; k < Cfg::NQL; ++k) {
-      const int c = tid + Cfg::NT * k;
-      const int o = tile_off<D>(c / CPR, c % CPR);
-      *reinterpret_cast<u32x4*>(&Qs[buf][o]) = qreg[k];
-      *reinterpret_cast<u32x4*>(&Os[buf][o]) = oreg[k];
+    for (int k = 0; k < Cfg::NL; ++k) {
+      const int c = tid + NT * k;
+      const int tns = c / (BQ * CPR), within = c % (BQ * CPR);
+      uint16_t* dst = tns ? Os[buf] : Qs[buf];
+      *reinterpret_cast<u32x4*>(&dst[tile_off<D>(within / CPR, within % CPR)]) = sreg[k];
     }
     if (tid < BQ)
       Ls[buf][tid] = lreg;
@@ -227,9 +234,9 @@ __global__ __launch_bounds__(256, EA_DKDV_MIN_WG) void dkdv_kernel(BwdParams p) 
       Ds[buf][tid - BQ] = lreg;
   };
 
-  const int swq = swz<D>(ln);                                  // Q/dO operand rows are ln
-  const int trow = 4 * g + ((lane & 15) >> 2);                 // transpose read: row within a 16-query step
-  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // transpose read: column within 32 dims
+  const int swq = swz<D>(l16);                 // Q/dO operand rows are 16*mb + l16
+  const int trow = 4 * g4 + (l16 >> 2);        // transpose read: query row (+16 for the second half)
+  const int tcol = 4 * (l16 & 3);              // transpose read: dim column within 16
 
   if (nt > 0) load_tile(tile_of(0));
 
@@ -246,7 +253,7 @@ __global__ __launch_bounds__(256, EA_DKDV_MIN_WG) void dkdv_kernel(BwdParams p) 
       const int iend = min(i0 + BQ, p.Sq);
       int qmn, qmx;
       seg_range(p.qs, i0, iend, qmn, qmx);
-      const bool tail = (i0 + BQ > p.Sq) || (kw0 + 32 > p.Sk);
+      const bool tail = (i0 + BQ > p.Sq) || (kw0 + 16 > p.Sk);
       if (!p.causal) cls = tail ? kPartial : kFull;
       else if (kmin_w > qmx) cls = kSkip;
       else if (kmax_w <= qmn && !tail) cls = kFull;
@@ -254,62 +261,58 @@ __global__ __launch_bounds__(256, EA_DKDV_MIN_WG) void dkdv_kernel(BwdParams p) 
     }
     if (cls == kSkip) continue;
 
-    // S = Q K^T and dP = dO V^T; lane = key, register r = query 8(r/4)+4g+r%4
-    f32x16 s = f32x16{}, dp = f32x16{};
-    {
-      const uint16_t* qrow = &Qs[buf][ln * D];
-      const uint16_t* orow = &Os[buf][ln * D];
+    // S = Q K^T and dP = dO V^T for two 16-query blocks; lane = key,
+    // register e of block mb = query 16*mb + 4*g4 + e
+    f32x4 s[2], dp[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb] = f32x4{};
+      dp[mb] = f32x4{};
+      const uint16_t* qrow = &Qs[buf][(16 * mb + l16) * D];
+      const uint16_t* orow = &Os[buf][(16 * mb + l16) * D];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const int o = ((2 * ks + g) ^ swq) << 3;
+        const int o = ((4 * ks + g4) ^ swq) << 3;
         const u32x4 aq = *reinterpret_cast<const u32x4*>(qrow + o);
-        s = mfma32(as_bf16x8(aq), kf[ks], s);
+        s[mb] = mfma16(as_bf16x8(aq), kf[ks], s[mb]);
         const u32x4 ao = *reinterpret_cast<const u32x4*>(orow + o);
-        dp = mfma32(as_bf16x8(ao), vf[ks], dp);
+        dp[mb] = mfma16(as_bf16x8(ao), vf[ks], dp[mb]);
       }
     }
 
-    f32x16 ds;
+    float pv[2][4], dsv[2][4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int qi = 8 * q4 + 4 * g;
+    for (int mb = 0; mb < 2; ++mb) {
+      const int qi = 16 * mb + 4 * g4;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][qi]);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][qi]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 4 * q4 + e;
-        float pv = fast_exp2(__builtin_fmaf(s[r], p.c, -l4[e]));
-        if (cls == kPartial) pv = in_window(qwin, i0 + qi + e) ? pv : 0.f;
-        s[r] = pv;
-        ds[r] = pv * (dp[r] - d4[e]);
+        float x = fast_exp2(__builtin_fmaf(s[mb][e], p.c, -l4[e]));
+        if (cls == kPartial) x = in_window(qwin, i0 + qi + e) ? x : 0.f;
+        pv[mb][e] = x;
+        dsv[mb][e] = x * (dp[mb][e] - d4[e]);
       }
     }
-    bf16x8 pb[2], sb[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int o = 8 * kk;
-      pb[kk] = pack_bf16x8(s[o], s[o + 1], s[o + 2], s[o + 3], s[o + 4], s[o + 5], s[o + 6], s[o + 7]);
-      sb[kk] = pack_bf16x8(ds[o], ds[o + 1], ds[o + 2], ds[o + 3], ds[o + 4], ds[o + 5], ds[o + 6], ds[o + 7]);
-    }
+    const bf16x8 pb = pack_bf16x8(pv[0][0], pv[0][1], pv[0][2], pv[0][3], pv[1][0], pv[1][1], pv[1][2], pv[1][3]);
+    const bf16x8 sb = pack_bf16x8(dsv[0][0], dsv[0][1], dsv[0][2], dsv[0][3], dsv[1][0], dsv[1][1], dsv[1][2],
+                                  dsv[1][3]);
 
-    // dV^T += dO^T P ; dK^T += Q^T dS   (reduction over the tile's 32 queries;
+    // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over the tile's 32 queries;
     // dO^T and Q^T read transposed from the row-major tiles)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int col = db * 32 + tcol;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int o0 = tile_off<D>(kk * 16 + trow, col >> 3) + (col & 7);
-        const int o1 = tile_off<D>(kk * 16 + 8 + trow, col >> 3) + (col & 7);
-        const u32x2 olo = ds_read_tr16(&Os[buf][o0]);
-        const u32x2 ohi = ds_read_tr16(&Os[buf][o1]);
-        const u32x4 ao = {olo[0], olo[1], ohi[0], ohi[1]};
-        dva[db] = mfma32(as_bf16x8(ao), pb[kk], dva[db]);
-        const u32x2 qlo = ds_read_tr16(&Qs[buf][o0]);
-        const u32x2 qhi = ds_read_tr16(&Qs[buf][o1]);
-        const u32x4 aq = {qlo[0], qlo[1], qhi[0], qhi[1]};
-        dka[db] = mfma32(as_bf16x8(aq), sb[kk], dka[db]);
-      }
+      const int col = 16 * db + tcol;
+      const int o0 = tile_off<D>(trow, col >> 3) + (col & 7);
+      const int o1 = tile_off<D>(16 + trow, col >> 3) + (col & 7);
+      const u32x2 olo = ds_read_tr16(&Os[buf][o0]);
+      const u32x2 ohi = ds_read_tr16(&Os[buf][o1]);
+      const u32x4 ao = {olo[0], olo[1], ohi[0], ohi[1]};
+      dva[db] = mfma16(as_bf16x8(ao), pb, dva[db]);
+      const u32x2 qlo = ds_read_tr16(&Qs[buf][o0]);
+      const u32x2 qhi = ds_read_tr16(&Qs[buf][o1]);
+      const u32x4 aq = {qlo[0], qlo[1], qhi[0], qhi[1]};
+      dka[db] = mfma16(as_bf16x8(aq), sb, dka[db]);
     }
   }
 
@@ -317,20 +320,18 @@ __global__ __launch_bounds__(256, EA_DKDV_MIN_WG) void dkdv_kernel(BwdParams p) 
   float* dkp = p.dk + b * p.k_bstride + (long)h * D_ + (long)krow * p.rs;
   float* dvp = p.dv + b * p.k_bstride + (long)h * D_ + (long)krow * p.rs;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db) {
+    const int d0 = 16 * db + 4 * g4;
+    f32x4 k4 = *reinterpret_cast<f32x4*>(dkp + d0);
+    f32x4 v4 = *reinterpret_cast<f32x4*>(dvp + d0);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = db * 32 + 8 * q4 + 4 * g;
-      f32x4 k4 = *reinterpret_cast<f32x4*>(dkp + d0);
-      f32x4 v4 = *reinterpret_cast<f32x4*>(dvp + d0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        k4[e] += p.scale * dka[db][4 * q4 + e];
-        v4[e] += dva[db][4 * q4 + e];
-      }
-      *reinterpret_cast<f32x4*>(dkp + d0) = k4;
-      *reinterpret_cast<f32x4*>(dvp + d0) = v4;
+    for (int e = 0; e < 4; ++e) {
+      k4[e] += p.scale * dka[db][e];
+      v4[e] += dva[db][e];
     }
+    *reinterpret_cast<f32x4*>(dkp + d0) = k4;
+    *reinterpret_cast<f32x4*>(dvp + d0) = v4;
+  }
 }
 
 // ------------------------------------------------------------------ dQ
@@ -572,10 +573,11 @@ hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   BwdParams p = make_params(a);
-  p.nblk = (a.Sk + 127) / 128;
+  const int bkv = DkdvCfg<128>::BKV;
+  p.nblk = (a.Sk + bkv - 1) / bkv;
   const long nwg = (long)a.B * a.H * p.nblk;
   if (nwg == 0 || a.Sq == 0) return hipSuccess;
-  dim3 grid((unsigned)nwg), block(256);
+  dim3 grid((unsigned)nwg), block(DkdvCfg<128>::NT);
   if (a.D == 64)
     hipLaunchKernelGGL(dkdv_kernel<64>, grid, block, 0, stream, p);
   else

@@ -26,6 +26,14 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, each holding the
+// 8 reduction indices 8*(l/16) .. 8*(l/16)+7 of the 32.  Output register r of
+// lane l holds D[4*(l/16) + r][l % 16].
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 
 // Round-to-nearest-even fp32 -> bf16 of two values, packed low/high.
