@@ -33,6 +33,9 @@
 #ifndef EA_DKDV_WAVES
 #define EA_DKDV_WAVES 8  // waves per dK/dV workgroup (16 keys each); 4 or 8
 #endif
+#ifndef EA_DKDV_BQ
+#define EA_DKDV_BQ 64  // query rows per dK/dV tile; 32 or 64
+#endif
 
 namespace ea {
 
@@ -103,18 +106,19 @@ __device__ __forceinline__ float lse_to_log2(float l) {
 // per SIMD.
 template <int D>
 struct DkdvCfg {
-  static constexpr int NW = EA_DKDV_WAVES, NT = 64 * NW, BKV = 16 * NW, BQ = 32;
+  static constexpr int NW = EA_DKDV_WAVES, NT = 64 * NW, BKV = 16 * NW, BQ = EA_DKDV_BQ;
+  static constexpr int NQB = BQ / 16, NKK = BQ / 32;  // 16-query score blocks, 32-query reduction steps
   static constexpr int CPR = D / 8;
   static constexpr int NL = 2 * BQ * CPR / NT;  // 16-byte chunks per thread per tile (Q and dO together)
   static constexpr int LDS_T = BQ * D;
-  static_assert(NL * NT == 2 * BQ * CPR && NL >= 1, "unsupported query tile");
+  static_assert(NL * NT == 2 * BQ * CPR && NL >= 1 && BQ % 32 == 0 && 2 * BQ <= NT, "unsupported query tile");
 };
 
 template <int D>
 __global__ __launch_bounds__(64 * EA_DKDV_WAVES, 8 / EA_DKDV_WAVES) void dkdv_kernel(BwdParams p) {
   using Cfg = DkdvCfg<D>;
   constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, CPR = Cfg::CPR, NT = Cfg::NT;
-  constexpr int NKS = D / 32, NDB = D / 16;
+  constexpr int NKS = D / 32, NDB = D / 16, NQB = Cfg::NQB, NKK = Cfg::NKK;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][Cfg::LDS_T];
   __shared__ __attribute__((aligned(16))) uint16_t Os[2][Cfg::LDS_T];   // dO
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
@@ -261,11 +265,11 @@ __global__ __launch_bounds__(64 * EA_DKDV_WAVES, 8 / EA_DKDV_WAVES) void dkdv_ke
     }
     if (cls == kSkip) continue;
 
-    // S = Q K^T and dP = dO V^T for two 16-query blocks; lane = key,
+    // S = Q K^T and dP = dO V^T for 16-query blocks; lane = key,
     // register e of block mb = query 16*mb + 4*g4 + e
-    f32x4 s[2], dp[2];
+    f32x4 s[NQB], dp[NQB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < NQB; ++mb) {
       s[mb] = f32x4{};
       dp[mb] = f32x4{};
       const uint16_t* qrow = &Qs[buf][(16 * mb + l16) * D];
@@ -280,9 +284,9 @@ __global__ __launch_bounds__(64 * EA_DKDV_WAVES, 8 / EA_DKDV_WAVES) void dkdv_ke
       }
     }
 
-    float pv[2][4], dsv[2][4];
+    float pv[NQB][4], dsv[NQB][4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < NQB; ++mb) {
       const int qi = 16 * mb + 4 * g4;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][qi]);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][qi]);
@@ -294,25 +298,31 @@ __global__ __launch_bounds__(64 * EA_DKDV_WAVES, 8 / EA_DKDV_WAVES) void dkdv_ke
         dsv[mb][e] = x * (dp[mb][e] - d4[e]);
       }
     }
-    const bf16x8 pb = pack_bf16x8(pv[0][0], pv[0][1], pv[0][2], pv[0][3], pv[1][0], pv[1][1], pv[1][2], pv[1][3]);
-    const bf16x8 sb = pack_bf16x8(dsv[0][0], dsv[0][1], dsv[0][2], dsv[0][3], dsv[1][0], dsv[1][1], dsv[1][2],
-                                  dsv[1][3]);
 
-    // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over the tile's 32 queries;
-    // dO^T and Q^T read transposed from the row-major tiles)
+    // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over 32 queries per step:
+    // query blocks 2*kk and 2*kk+1; dO^T and Q^T read transposed from the
+    // row-major tiles)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int col = 16 * db + tcol;
-      const int o0 = tile_off<D>(trow, col >> 3) + (col & 7);
-      const int o1 = tile_off<D>(16 + trow, col >> 3) + (col & 7);
-      const u32x2 olo = ds_read_tr16(&Os[buf][o0]);
-      const u32x2 ohi = ds_read_tr16(&Os[buf][o1]);
-      const u32x4 ao = {olo[0], olo[1], ohi[0], ohi[1]};
-      dva[db] = mfma16(as_bf16x8(ao), pb, dva[db]);
-      const u32x2 qlo = ds_read_tr16(&Qs[buf][o0]);
-      const u32x2 qhi = ds_read_tr16(&Qs[buf][o1]);
-      const u32x4 aq = {qlo[0], qlo[1], qhi[0], qhi[1]};
-      dka[db] = mfma16(as_bf16x8(aq), sb, dka[db]);
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int m0 = 2 * kk, m1 = 2 * kk + 1;
+      const bf16x8 pb = pack_bf16x8(pv[m0][0], pv[m0][1], pv[m0][2], pv[m0][3], pv[m1][0], pv[m1][1], pv[m1][2],
+                                    pv[m1][3]);
+      const bf16x8 sb = pack_bf16x8(dsv[m0][0], dsv[m0][1], dsv[m0][2], dsv[m0][3], dsv[m1][0], dsv[m1][1],
+                                    dsv[m1][2], dsv[m1][3]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = 16 * db + tcol;
+        const int o0 = tile_off<D>(32 * kk + trow, col >> 3) + (col & 7);
+        const int o1 = tile_off<D>(32 * kk + 16 + trow, col >> 3) + (col & 7);
+        const u32x2 olo = ds_read_tr16(&Os[buf][o0]);
+        const u32x2 ohi = ds_read_tr16(&Os[buf][o1]);
+        const u32x4 ao = {olo[0], olo[1], ohi[0], ohi[1]};
+        dva[db] = mfma16(as_bf16x8(ao), pb, dva[db]);
+        const u32x2 qlo = ds_read_tr16(&Qs[buf][o0]);
+        const u32x2 qhi = ds_read_tr16(&Qs[buf][o1]);
+        const u32x4 aq = {qlo[0], qlo[1], qhi[0], qhi[1]};
+        dka[db] = mfma16(as_bf16x8(aq), sb, dka[db]);
+      }
     }
   }
 

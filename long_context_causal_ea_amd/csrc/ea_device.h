@@ -36,11 +36,14 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 
-// Round-to-nearest-even fp32 -> bf16 of two values, packed low/high.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed low/high (one
+// v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 pack_bf16x8(float x0, float x1, float x2, float x3, float x4, float x5,
@@ -54,16 +57,20 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float x0, float x1, float x2, floa
 }
 
 // ---- LDS tiles: row-major [rows][D] bf16, 16-byte chunks XOR-swizzled per row.
-// Chunk c of row r is stored at chunk slot c ^ swz(r).  The swizzle keeps both
+// Chunk c of row r is stored at chunk slot c ^ swz(r).  The swizzle keeps the
 // access patterns of the kernels free of bank conflicts on 64 banks x 4 bytes:
 // (a) 16 lanes reading the same chunk of 16 consecutive rows (MFMA operands
-// whose reduction index runs along D), and (b) the transpose reads below, where
-// 32 lanes read 4 consecutive rows x 64 bytes.
+// whose reduction index runs along D), (b) transpose reads (below) where 32
+// lanes read 4 consecutive rows x 64 bytes (32x32 MFMA operands) and (c) where
+// 32 lanes read 8 consecutive rows x 32 bytes (16x16 MFMA operands).  For 16
+// chunks per row that asks for a permutation of the row's low 4 bits whose top
+// 2 bits differ across any aligned 4 rows and top 3 bits across any aligned 8
+// rows: the 3-bit reversal of r mod 8, then bit 3 of r.
 template <int D>
 __device__ __forceinline__ int swz(int r);
 template <>
 __device__ __forceinline__ int swz<128>(int r) {  // 16 chunks per row
-  return ((r & 3) << 2) | ((r >> 2) & 3);
+  return ((r & 1) << 3) | (r & 2) << 1 | ((r >> 2) & 1) << 1 | ((r >> 3) & 1);
 }
 template <>
 __device__ __forceinline__ int swz<64>(int r) {  // 8 chunks per row, two rows per 256 bytes

@@ -19,6 +19,8 @@
 //    pair), FULL (all allowed, no mask work) or PARTIAL (element mask; also
 //    ragged key tails).  Tiles no query of the workgroup may see are never
 //    loaded.
+#include <type_traits>
+
 #include "ea_device.h"
 #include "ea_launch.h"
 
@@ -150,15 +152,29 @@ __global__ __launch_bounds__(256, EA_FWD_MIN_WG) void fwd_kernel(FwdParams p) {
     }
   };
 
-  // per-lane pieces of the LDS addresses
-  const int swk = swz<D>(ln);                                  // K operand rows are mb*32 + ln
-  const int trow = 4 * g + ((lane & 15) >> 2);                 // transpose read: row within a 16-key step
-  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // transpose read: column within 32 dims
+  // per-lane LDS offsets (elements), fixed for the whole kernel: with the tile
+  // buffer, the 32-key block and the 16-key step folded in as immediates, no
+  // address arithmetic is left in the loop
+  int kofs[NKS];  // K operand: row ln, chunk 2*ks+g
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) kofs[ks] = ln * D + (((2 * ks + g) ^ swz<D>(ln)) << 3);
+  int vofs[2][NDB];  // V^T transpose read: rows 8*half + trow (+16 per step), 32 dims per block
+  {
+    const int trow = 4 * g + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = 32 * db + tcol;
+        vofs[half][db] = tile_off<D>(8 * half + trow, col >> 3) + (col & 7);
+      }
+  }
 
-  if (nt > 0) load_tile(tile_of(0));
-
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
+  // one key tile: classify, scores, online softmax, P V.  BUF is a compile-time
+  // buffer index so that every LDS offset is an immediate.
+  auto tile_step = [&](auto BUF, int t) {
+    constexpr int buf = decltype(BUF)::value;
     const int jt = tile_of(t);
     const int j0 = jt * BK;
     store_tile(buf);
@@ -177,17 +193,16 @@ __global__ __launch_bounds__(256, EA_FWD_MIN_WG) void fwd_kernel(FwdParams p) {
       else if (kmx <= qmin_w && !tail) cls = kFull;
       else cls = kPartial;
     }
-    if (cls == kSkip) continue;
+    if (cls == kSkip) return;
 
     // S^T = K Q^T, one 32-key MFMA block at a time
     f32x16 st[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       st[mb] = f32x16{};
-      const uint16_t* krow = &Ks[buf][(mb * 32 + ln) * D];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + (((2 * ks + g) ^ swk) << 3));
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[buf][kofs[ks] + mb * 32 * D]);
         st[mb] = mfma32(as_bf16x8(a), qf[ks], st[mb]);
       }
     }
@@ -239,16 +254,20 @@ __global__ __launch_bounds__(256, EA_FWD_MIN_WG) void fwd_kernel(FwdParams p) {
     // O^T += V^T P^T; V^T read transposed from the row-major V tile
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int col = db * 32 + tcol;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const int r0 = kb * 16 + trow, r1 = r0 + 8;
-        const u32x2 lo = ds_read_tr16(&Vs[buf][tile_off<D>(r0, col >> 3) + (col & 7)]);
-        const u32x2 hi = ds_read_tr16(&Vs[buf][tile_off<D>(r1, col >> 3) + (col & 7)]);
+        const u32x2 lo = ds_read_tr16(&Vs[buf][vofs[0][db] + kb * 16 * D]);
+        const u32x2 hi = ds_read_tr16(&Vs[buf][vofs[1][db] + kb * 16 * D]);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         oacc[db] = mfma32(as_bf16x8(a), pb[kb], oacc[db]);
       }
     }
+  };
+
+  if (nt > 0) load_tile(tile_of(0));
+  for (int t = 0; t < nt; t += 2) {
+    tile_step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < nt) tile_step(std::integral_constant<int, 1>{}, t + 1);
   }
 
   // ---- epilogue: normalise, write O and LSE
