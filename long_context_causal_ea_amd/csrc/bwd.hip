@@ -124,7 +124,8 @@ __global__ __launch_bounds__(64 * EA_DKDV_WAVES, 8 / EA_DKDV_WAVES) void dkdv_ke
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
   const int l16 = lane & 15, g4 = lane >> 4;
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
@@ -363,7 +364,8 @@ __global__ __launch_bounds__(256, EA_DQ_MIN_WG) void dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][Cfg::LDS_T];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][Cfg::LDS_T];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
   const int ln = lane & 31, g = lane >> 5;
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);

@@ -91,6 +91,27 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Direct global -> LDS load of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane i's 16 bytes land at LDS byte address lds_base + 16*i (lds_base must be
+// the same for the whole wave).  Issued as inline assembly on purpose: the
+// compiler would otherwise wait for every such load in flight before any later
+// LDS read, which defeats a multi-stage ring.  Callers therefore own the
+// ordering: "s_waitcnt vmcnt(n)" for their own loads, then a workgroup barrier,
+// then a compiler memory fence (lds_ring_sync below) before reading the data.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)lds_base);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
+}
+
+// Wait until at most N direct-to-LDS loads of this wave are in flight, then
+// synchronise the workgroup; afterwards every wave sees the completed loads.
+template <int N>
+__device__ __forceinline__ void lds_ring_sync() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // Exponent base 2 on the hardware transcendental unit.

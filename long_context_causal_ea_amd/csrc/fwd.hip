@@ -5,8 +5,10 @@
 //
 // gfx950 mapping
 //  - One workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-//    owns 32 rows.  Key/value tiles of 64 rows stream through LDS, double
-//    buffered, with the next tile's global loads in flight during compute.
+//    owns 32 rows.  Key/value tiles of 32 rows stream through a ring of LDS
+//    stages filled by direct global->LDS loads, three tiles in flight.
+//  - The loop is software-pipelined: the scores of tile t+1 are issued to the
+//    matrix cores while the softmax of tile t runs on the vector ALUs.
 //  - Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
 //    every lane then holds 32 scores of ONE query row, so the row max and row
 //    sum are in-lane reductions plus one exchange with lane l^32.
@@ -40,32 +42,32 @@ struct FwdParams {
   float scale, c;  // c = scale * log2(e)
 };
 
-#ifndef EA_FWD_BK
-#define EA_FWD_BK 64
-#endif
-#ifndef EA_FWD_MIN_WG
-#define EA_FWD_MIN_WG 2  // workgroups per CU the register budget is sized for
+#ifndef EA_FWD_NST
+#define EA_FWD_NST 4  // LDS stages of the key/value ring (tiles in flight: NST - 1)
 #endif
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BQ = 128, BK = EA_FWD_BK, NT = 256;
-  static constexpr int NMB = BK / 32, NKB = BK / 16;  // 32-key MFMA blocks, 16-key reduction steps
-  static constexpr int CPR = D / 8;  // 16-byte chunks per row
-  static constexpr int NKL = BK * CPR / NT;  // chunks per thread per tile (each of K and V)
+  static constexpr int BQ = 128, BK = 32, NT = 256, NST = EA_FWD_NST;
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;       // rows one wave covers per direct-to-LDS load
+  static constexpr int NKL = BK / (4 * RPI); // direct-to-LDS loads per thread per tile (each of K and V)
   static constexpr int LDS_T = BK * D;
-  static_assert(BK % 32 == 0 && NKL * NT == BK * CPR, "unsupported key tile");
+  static_assert(NKL >= 1 && NKL * 4 * RPI == BK, "unsupported key tile");
 };
 
+// Rows of a key/value tile that lie past the end of the keys load the last key
+// row instead (so every address is valid); the score mask removes them.
 template <int D>
-__global__ __launch_bounds__(256, EA_FWD_MIN_WG) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   using Cfg = FwdCfg<D>;
-  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, CPR = Cfg::CPR;
-  constexpr int NKS = D / 16, NDB = D / 32, NMB = Cfg::NMB, NKB = Cfg::NKB;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][Cfg::LDS_T];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][Cfg::LDS_T];
+  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, CPR = Cfg::CPR, NST = Cfg::NST, RPI = Cfg::RPI;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NST][Cfg::LDS_T];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NST][Cfg::LDS_T];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
   const int ln = lane & 31, g = lane >> 5;
 
   // ---- work item: (batch*head) major, longest query blocks first
@@ -92,6 +94,10 @@ __global__ __launch_bounds__(256, EA_FWD_MIN_WG) void fwd_kernel(FwdParams p) {
       u32x4 u = row_ok ? src[2 * ks] : u32x4{0u, 0u, 0u, 0u};
       qf[ks] = as_bf16x8(u);
     }
+    // land the Q rows before the direct-to-LDS ring starts: the compiler cannot
+    // see those loads and would otherwise wait for all of them at each use of Q
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qf[ks]));
   }
   const int qpos = seg_pos(p.qs, row_ok ? qrow : (p.Sq - 1));
   const KeyWindow kwin = key_window(p.ks, qpos, p.causal);
@@ -114,47 +120,50 @@ __global__ __launch_bounds__(256, EA_FWD_MIN_WG) void fwd_kernel(FwdParams p) {
   if (tB0 < nA) tB0 = nA;
   const int nB = tB1 > tB0 ? tB1 - tB0 : 0;
   const int nt = nA + nB;
+  auto tile_of = [&](int t) { return t < nA ? t : tB0 + (t - nA); };
 
   // ---- running statistics (raw-score units for the max)
   constexpr float NEG_INF = -__builtin_inff();
+  // The running maximum is raised only when a tile's maximum exceeds it by more
+  // than 8 (in log2 units): probabilities then stay below 2^8, exactly
+  // representable in the accumulation, and the rescale of O is rare.
+  const float raise_thr = 8.f / p.c;
   float m_run = NEG_INF, l_run = 0.f;
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
 
-  u32x4 kreg[Cfg::NKL], vreg[Cfg::NKL];
-
-  auto tile_of = [&](int t) { return t < nA ? t : tB0 + (t - nA); };
-
-  // global -> registers: consecutive threads take consecutive 16-byte chunks of a row
-  auto load_tile = [&](int jt) {
-    const int j0 = jt * BK;
+  // ---- direct global -> LDS loads: one instruction moves 16 bytes per lane into
+  // 64 consecutive 16-byte LDS slots (RPI rows); lane i fills slot i % CPR of row
+  // i / CPR, i.e. chunk (slot ^ swz(row)) of that row in the swizzled layout.
+  const int dma_row = lane / CPR, dma_slot = lane % CPR;
+  long dma_off[Cfg::NKL];  // element offset of this lane's 16 bytes within a tile whose first row is 0
+#pragma unroll
+  for (int it = 0; it < Cfg::NKL; ++it) {
+    const int row = RPI * (w + 4 * it) + dma_row;
+    dma_off[it] = (long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3);
+  }
+  auto issue_tile = [&](auto STAGE, int t) {
+    constexpr int stage = decltype(STAGE)::value;
+    const int tt = t < nt ? t : nt - 1;  // past the end: reload the last tile into a stage nobody reads
+    const int j0 = tile_of(tt) * BK;
+    const bool whole = j0 + BK <= p.Sk;
 #pragma unroll
     for (int it = 0; it < Cfg::NKL; ++it) {
-      const int c = tid + Cfg::NT * it;
-      const int row = c / CPR, col = c % CPR;
-      const int j = j0 + row;
-      const long off = (long)j * p.rs + col * 8;
-      kreg[it] = j < p.Sk ? *reinterpret_cast<const u32x4*>(kp + off) : u32x4{0u, 0u, 0u, 0u};
-      vreg[it] = j < p.Sk ? *reinterpret_cast<const u32x4*>(vp + off) : u32x4{0u, 0u, 0u, 0u};
+      const int row0 = RPI * (w + 4 * it);
+      long off = (long)j0 * p.rs + dma_off[it];
+      if (!whole) {
+        const int row = row0 + dma_row;
+        const int j = min(j0 + row, p.Sk - 1);
+        off = (long)j * p.rs + ((dma_slot ^ swz<D>(row)) << 3);
+      }
+      dma16(kp + off, &Ks[stage][row0 * D]);
+      dma16(vp + off, &Vs[stage][row0 * D]);
     }
   };
+  constexpr int LOADS_PER_TILE = 2 * Cfg::NKL;
 
-  // registers -> LDS, swizzled row-major
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < Cfg::NKL; ++it) {
-      const int c = tid + Cfg::NT * it;
-      const int row = c / CPR, col = c % CPR;
-      const int o = tile_off<D>(row, col);
-      *reinterpret_cast<u32x4*>(&Ks[buf][o]) = kreg[it];
-      *reinterpret_cast<u32x4*>(&Vs[buf][o]) = vreg[it];
-    }
-  };
-
-  // per-lane LDS offsets (elements), fixed for the whole kernel: with the tile
-  // buffer, the 32-key block and the 16-key step folded in as immediates, no
-  // address arithmetic is left in the loop
+  // per-lane LDS offsets (elements), fixed for the whole kernel
   int kofs[NKS];  // K operand: row ln, chunk 2*ks+g
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) kofs[ks] = ln * D + (((2 * ks + g) ^ swz<D>(ln)) << 3);
@@ -171,103 +180,119 @@ __global__ __launch_bounds__(256, EA_FWD_MIN_WG) void fwd_kernel(FwdParams p) {
       }
   }
 
-  // one key tile: classify, scores, online softmax, P V.  BUF is a compile-time
-  // buffer index so that every LDS offset is an immediate.
-  auto tile_step = [&](auto BUF, int t) {
-    constexpr int buf = decltype(BUF)::value;
-    const int jt = tile_of(t);
-    const int j0 = jt * BK;
-    store_tile(buf);
-    __syncthreads();
-    if (t + 1 < nt) load_tile(tile_of(t + 1));
+  // wave-level class of tile t
+  auto classify = [&](int t) {
+    if (!wave_live) return (int)kSkip;
+    const int j0 = tile_of(t) * BK;
+    const int jend = min(j0 + BK, p.Sk);
+    int kmn, kmx;
+    seg_range(p.ks, j0, jend, kmn, kmx);
+    const bool tail = j0 + BK > p.Sk;
+    if (!p.causal) return tail ? (int)kPartial : (int)kFull;
+    if (kmn > qmax_w) return (int)kSkip;
+    if (kmx <= qmin_w && !tail) return (int)kFull;
+    return (int)kPartial;
+  };
 
-    // wave-level tile class
-    int cls = kSkip;
-    if (wave_live) {
-      const int jend = min(j0 + BK, p.Sk);
-      int kmn, kmx;
-      seg_range(p.ks, j0, jend, kmn, kmx);
-      const bool tail = j0 + BK > p.Sk;
-      if (!p.causal) cls = tail ? kPartial : kFull;
-      else if (kmn > qmax_w) cls = kSkip;
-      else if (kmx <= qmin_w && !tail) cls = kFull;
-      else cls = kPartial;
+  // S^T = K Q^T of the tile in stage STAGE
+  auto scores = [&](auto STAGE) {
+    constexpr int stage = decltype(STAGE)::value;
+    f32x16 st = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[stage][kofs[ks]]);
+      st = mfma32(as_bf16x8(a), qf[ks], st);
     }
-    if (cls == kSkip) return;
+    return st;
+  };
 
-    // S^T = K Q^T, one 32-key MFMA block at a time
-    f32x16 st[NMB];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      st[mb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[buf][kofs[ks] + mb * 32 * D]);
-        st[mb] = mfma32(as_bf16x8(a), qf[ks], st[mb]);
-      }
-    }
+  using I0 = std::integral_constant<int, 0>;
 
-    if (cls == kPartial) {
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
+  // one pipeline step: softmax and P V of tile t (scores in st_cur, stage STAGE)
+  // interleaved with the scores of tile t+1 (into st_next, stage STAGE+1)
+  auto step = [&](auto STAGE, int t, f32x16& st_cur, int& cls_cur, f32x16& st_next, int& cls_next) {
+    constexpr int stage = decltype(STAGE)::value;
+    constexpr int nstage = (stage + 1) % NST, fstage = (stage + NST - 1) % NST;
+    // tile t+1 resident for every wave; everyone is done with stage (t-1) % NST
+    lds_ring_sync<(NST - 3) * LOADS_PER_TILE>();
+    issue_tile(std::integral_constant<int, fstage>{}, t + NST - 1);
+    const int j0 = tile_of(t) * BK;
+    const bool has_next = t + 1 < nt;
+    cls_next = has_next ? classify(t + 1) : (int)kSkip;
+
+    if (cls_cur != kSkip) {
+      if (cls_cur == kPartial) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = j0 + mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          st[mb][r] = in_window(kwin, j) ? st[mb][r] : NEG_INF;
+          const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          st_cur[r] = in_window(kwin, j) ? st_cur[r] : NEG_INF;
         }
       }
+      float mx = NEG_INF;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st_cur[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (__any(mx > m_run + raise_thr)) {
+        const float mnew = fmaxf(m_run, mx);
+        const float alpha = (m_run == NEG_INF) ? 0.f : fast_exp2((m_run - mnew) * p.c);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        m_run = mnew;
+      }
     }
 
-    // online softmax: tile max, conditional rescale, exponentials, partial sums
-    float mx = NEG_INF;
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m_run, mx);
-    if (__any(mnew > m_run)) {
-      const float alpha = (m_run == NEG_INF) ? 0.f : fast_exp2((m_run - mnew) * p.c);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      m_run = mnew;
-    }
-    const float msub = (m_run == NEG_INF) ? 0.f : m_run * p.c;
-    bf16x8 pb[NKB];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
+    // scores of the next tile (independent of the softmax below: the two interleave)
+    if (cls_next != kSkip) st_next = scores(std::integral_constant<int, nstage>{});
+
+    if (cls_cur != kSkip) {
+      const float msub = (m_run == NEG_INF) ? 0.f : m_run * p.c;
+      float e[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(__builtin_fmaf(st[mb][r], p.c, -msub));
-        st[mb][r] = e;
-        l_run += e;
+        e[r] = fast_exp2(__builtin_fmaf(st_cur[r], p.c, -msub));
+        l_run += e[r];
       }
+      const bf16x8 pb0 = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      const bf16x8 pb1 = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+      // O^T += V^T P^T; V^T read transposed from the row-major V tile
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int o = 8 * kk;
-        pb[2 * mb + kk] = pack_bf16x8(st[mb][o + 0], st[mb][o + 1], st[mb][o + 2], st[mb][o + 3], st[mb][o + 4],
-                                      st[mb][o + 5], st[mb][o + 6], st[mb][o + 7]);
-      }
-    }
-
-    // O^T += V^T P^T; V^T read transposed from the row-major V tile
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x2 lo = ds_read_tr16(&Vs[buf][vofs[0][db] + kb * 16 * D]);
-        const u32x2 hi = ds_read_tr16(&Vs[buf][vofs[1][db] + kb * 16 * D]);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = mfma32(as_bf16x8(a), pb[kb], oacc[db]);
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2 lo0 = ds_read_tr16(&Vs[stage][vofs[0][db]]);
+        const u32x2 hi0 = ds_read_tr16(&Vs[stage][vofs[1][db]]);
+        const u32x2 lo1 = ds_read_tr16(&Vs[stage][vofs[0][db] + 16 * D]);
+        const u32x2 hi1 = ds_read_tr16(&Vs[stage][vofs[1][db] + 16 * D]);
+        const u32x4 a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
+        const u32x4 a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
+        oacc[db] = mfma32(as_bf16x8(a0), pb0, oacc[db]);
+        oacc[db] = mfma32(as_bf16x8(a1), pb1, oacc[db]);
       }
     }
   };
 
-  if (nt > 0) load_tile(tile_of(0));
-  for (int t = 0; t < nt; t += 2) {
-    tile_step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < nt) tile_step(std::integral_constant<int, 1>{}, t + 1);
+  if (nt > 0) {
+    // prologue: NST-1 tiles in flight, scores of tile 0
+    static_assert(NST == 4, "the loop below is unrolled for a ring of 4 stages");
+    issue_tile(std::integral_constant<int, 0>{}, 0);
+    issue_tile(std::integral_constant<int, 1>{}, 1);
+    issue_tile(std::integral_constant<int, 2>{}, 2);
+    lds_ring_sync<(NST - 2) * LOADS_PER_TILE>();
+    int cls_a = classify(0), cls_b = kSkip;
+    f32x16 st_a = f32x16{}, st_b = f32x16{};
+    if (cls_a != kSkip) st_a = scores(I0{});
+
+    // unrolled by the ring size so that every stage index is a constant and the
+    // two score buffers alternate without copies
+    for (int t = 0; t < nt; t += 4) {
+      step(std::integral_constant<int, 0>{}, t, st_a, cls_a, st_b, cls_b);
+      if (t + 1 >= nt) break;
+      step(std::integral_constant<int, 1>{}, t + 1, st_b, cls_b, st_a, cls_a);
+      if (t + 2 >= nt) break;
+      step(std::integral_constant<int, 2>{}, t + 2, st_a, cls_a, st_b, cls_b);
+      if (t + 3 >= nt) break;
+      step(std::integral_constant<int, 3>{}, t + 3, st_b, cls_b, st_a, cls_a);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // retire the trailing (unused) loads
   }
 
   // ---- epilogue: normalise, write O and LSE
