@@ -42,6 +42,9 @@ struct FwdParams {
   float scale, c;  // c = scale * log2(e)
 };
 
+#ifndef EA_FWD_LDS_AHEAD
+#define EA_FWD_LDS_AHEAD 0  // >0: schedule hints with this many LDS reads ahead (0: compiler default)
+#endif
 #ifndef EA_FWD_NST
 #define EA_FWD_NST 4  // LDS stages of the key/value ring (tiles in flight: NST - 1)
 #endif
@@ -164,9 +167,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int LOADS_PER_TILE = 2 * Cfg::NKL;
 
   // per-lane LDS offsets (elements), fixed for the whole kernel
-  int kofs[NKS];  // K operand: row ln, chunk 2*ks+g
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) kofs[ks] = ln * D + (((2 * ks + g) ^ swz<D>(ln)) << 3);
+  // K operand: row ln, chunk 2*ks+g, i.e. slot (2*ks+g) ^ swz(ln) = 2*(ks ^ kx) + kg
+  const int kx = swz<D>(ln) >> 1, kbase = ln * D + ((g ^ (swz<D>(ln) & 1)) << 3);
   int vofs[2][NDB];  // V^T transpose read: rows 8*half + trow (+16 per step), 32 dims per block
   {
     const int trow = 4 * g + ((lane & 15) >> 2);
@@ -180,18 +182,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       }
   }
 
-  // wave-level class of tile t
+  // wave-level class of tile t: FULL (no mask needed) or PARTIAL (element mask).
+  // A tile with no allowed pair for this wave is computed as PARTIAL (all of it
+  // masked): that keeps the loop one straight pipeline, and such tiles are the
+  // few past each wave's diagonal.
   auto classify = [&](int t) {
-    if (!wave_live) return (int)kSkip;
     const int j0 = tile_of(t) * BK;
-    const int jend = min(j0 + BK, p.Sk);
+    if (!wave_live || j0 + BK > p.Sk) return (int)kPartial;
+    if (!p.causal) return (int)kFull;
     int kmn, kmx;
-    seg_range(p.ks, j0, jend, kmn, kmx);
-    const bool tail = j0 + BK > p.Sk;
-    if (!p.causal) return tail ? (int)kPartial : (int)kFull;
-    if (kmn > qmax_w) return (int)kSkip;
-    if (kmx <= qmin_w && !tail) return (int)kFull;
-    return (int)kPartial;
+    seg_range(p.ks, j0, j0 + BK, kmn, kmx);
+    return kmx <= qmin_w ? (int)kFull : (int)kPartial;
   };
 
   // S^T = K Q^T of the tile in stage STAGE
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     f32x16 st = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[stage][kofs[ks]]);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[stage][kbase + ((ks ^ kx) << 4)]);
       st = mfma32(as_bf16x8(a), qf[ks], st);
     }
     return st;
@@ -218,56 +219,70 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     issue_tile(std::integral_constant<int, fstage>{}, t + NST - 1);
     const int j0 = tile_of(t) * BK;
     const bool has_next = t + 1 < nt;
-    cls_next = has_next ? classify(t + 1) : (int)kSkip;
+    cls_next = has_next ? classify(t + 1) : (int)kFull;
 
-    if (cls_cur != kSkip) {
-      if (cls_cur == kPartial) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          st_cur[r] = in_window(kwin, j) ? st_cur[r] : NEG_INF;
-        }
-      }
-      float mx = NEG_INF;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st_cur[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (__any(mx > m_run + raise_thr)) {
-        const float mnew = fmaxf(m_run, mx);
-        const float alpha = (m_run == NEG_INF) ? 0.f : fast_exp2((m_run - mnew) * p.c);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-        m_run = mnew;
-      }
-    }
-
-    // scores of the next tile (independent of the softmax below: the two interleave)
-    if (cls_next != kSkip) st_next = scores(std::integral_constant<int, nstage>{});
-
-    if (cls_cur != kSkip) {
-      const float msub = (m_run == NEG_INF) ? 0.f : m_run * p.c;
-      float e[16];
+    if (cls_cur == kPartial) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        e[r] = fast_exp2(__builtin_fmaf(st_cur[r], p.c, -msub));
-        l_run += e[r];
-      }
-      const bf16x8 pb0 = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-      const bf16x8 pb1 = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
-      // O^T += V^T P^T; V^T read transposed from the row-major V tile
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2 lo0 = ds_read_tr16(&Vs[stage][vofs[0][db]]);
-        const u32x2 hi0 = ds_read_tr16(&Vs[stage][vofs[1][db]]);
-        const u32x2 lo1 = ds_read_tr16(&Vs[stage][vofs[0][db] + 16 * D]);
-        const u32x2 hi1 = ds_read_tr16(&Vs[stage][vofs[1][db] + 16 * D]);
-        const u32x4 a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
-        const u32x4 a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
-        oacc[db] = mfma32(as_bf16x8(a0), pb0, oacc[db]);
-        oacc[db] = mfma32(as_bf16x8(a1), pb1, oacc[db]);
+        const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        st_cur[r] = in_window(kwin, j) ? st_cur[r] : NEG_INF;
       }
     }
+    float mx = NEG_INF;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st_cur[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_run + raise_thr)) {
+      const float mnew = fmaxf(m_run, mx);
+      const float alpha = (m_run == NEG_INF) ? 0.f : fast_exp2((m_run - mnew) * p.c);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      m_run = mnew;
+    }
+
+    // One straight-line block: the scores of tile t+1 (matrix cores) do not
+    // depend on the softmax of tile t (vector ALUs), so the two interleave.  On
+    // the last tile the scores of a dummy tile are computed and dropped.
+    st_next = scores(std::integral_constant<int, nstage>{});
+    const float msub = (m_run == NEG_INF) ? 0.f : m_run * p.c;
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      e[r] = fast_exp2(__builtin_fmaf(st_cur[r], p.c, -msub));
+      l_run += e[r];
+    }
+    const bf16x8 pb0 = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    const bf16x8 pb1 = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+    // O^T += V^T P^T; V^T read transposed from the row-major V tile
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const u32x2 lo0 = ds_read_tr16(&Vs[stage][vofs[0][db]]);
+      const u32x2 hi0 = ds_read_tr16(&Vs[stage][vofs[1][db]]);
+      const u32x2 lo1 = ds_read_tr16(&Vs[stage][vofs[0][db] + 16 * D]);
+      const u32x2 hi1 = ds_read_tr16(&Vs[stage][vofs[1][db] + 16 * D]);
+      const u32x4 a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
+      const u32x4 a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
+      oacc[db] = mfma32(as_bf16x8(a0), pb0, oacc[db]);
+      oacc[db] = mfma32(as_bf16x8(a1), pb1, oacc[db]);
+    }
+    // schedule: LDS reads run EA_FWD_LDS_AHEAD operands ahead of the MFMAs that
+    // consume them; NKS x {1 MFMA, 1 LDS read, 7 VALU} (scores + softmax), then
+    // 2*NDB x {1 MFMA, 2 LDS transpose reads} (P V)
+#if EA_FWD_LDS_AHEAD > 0
+    __builtin_amdgcn_sched_group_barrier(0x100, EA_FWD_LDS_AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * NDB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#endif
   };
 
   if (nt > 0) {
@@ -277,9 +292,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     issue_tile(std::integral_constant<int, 1>{}, 1);
     issue_tile(std::integral_constant<int, 2>{}, 2);
     lds_ring_sync<(NST - 2) * LOADS_PER_TILE>();
-    int cls_a = classify(0), cls_b = kSkip;
-    f32x16 st_a = f32x16{}, st_b = f32x16{};
-    if (cls_a != kSkip) st_a = scores(I0{});
+    int cls_a = classify(0), cls_b = kFull;
+    f32x16 st_a = scores(I0{}), st_b;
 
     // unrolled by the ring size so that every stage index is a constant and the
     // two score buffers alternate without copies
