@@ -28,6 +28,6 @@ tiny inputs, torch fp64 autograd, finite differences, closed forms, exact
 invariants (key-split merge, zigzag reassembly) and hand-derived fixtures.
 """
 from .attention import (  # noqa: F401
-    allowed_mask, attn_fwd, attn_bwd, lse_merge, attn_fwd_heads, attn_bwd_heads,
+    allowed_mask, allowed_sums, attn_fwd, attn_bwd, lse_merge, attn_fwd_heads, attn_bwd_heads,
 )
 from .zigzag import zigzag_positions, ring_source, chunk_positions  # noqa: F401

@@ -59,6 +59,25 @@ def allowed_mask(pos_q, pos_k, causal: bool) -> np.ndarray:
     return pos_k[None, :] <= pos_q[:, None]
 
 
+def allowed_sums(pos_q, pos_k, causal: bool, weights) -> np.ndarray:
+    """Per query row i: sum over the keys j allowed for i of weights[j] (weights [Sk, C]).
+
+    Same rule as allowed_mask, evaluated for long sequences without forming the
+    mask: keys sorted by position, prefix sums, and for each query the number of
+    keys with pos_k <= pos_q(i).  Exact for integer weights.
+    """
+    pos_q = np.asarray(pos_q, dtype=np.int64)
+    pos_k = np.asarray(pos_k, dtype=np.int64)
+    w = np.asarray(weights, dtype=np.int64).reshape(pos_k.shape[0], -1)
+    total = w.sum(axis=0)
+    if not causal:
+        return np.broadcast_to(total, (pos_q.shape[0], w.shape[1])).copy()
+    order = np.argsort(pos_k, kind="stable")
+    csum = np.concatenate([np.zeros((1, w.shape[1]), dtype=np.int64), np.cumsum(w[order], axis=0)])
+    n = np.searchsorted(pos_k[order], pos_q, side="right")
+    return csum[n]
+
+
 def _row_blocks(sq: int, sk: int, budget_elems: int = 1 << 24):
     rows = max(1, min(sq, budget_elems // max(1, sk)))
     for i0 in range(0, sq, rows):

@@ -1,0 +1,135 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench times.
+
+The whole workload (all heads, full sequence) runs on the GPU exactly as in
+bench.py.  The fp64 oracle then checks, per workload:
+  * every output of a few whole heads where that finishes in seconds (C2), or
+  * sampled query rows (O, LSE, dQ; each row's oracle cost is one pass over its
+    keys) and sampled key rows whose attending queries are few (dK, dV), and
+  * properties that hold at any size: keys nobody may see get dK = dV = 0
+    exactly; sum_j dK_j = 0; sum_j dV_j = sum of dO over rows with keys.
+Bars: max-abs <= 1e-2 and relative L2 <= 5e-3 on O, dQ, dK, dV (fp32 outputs);
+LSE within 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import long_context_causal_ea_amd as ea
+import synth
+from tests.parity import assert_close, assert_lse, banner, to_np
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+DEV = "cuda"
+
+
+def _head_np(x, h):
+    return x[0, :, h].double().cpu().numpy()
+
+
+def _run_dense(cfg):
+    t = synth.make_dense_case(cfg, DEV)
+    drv = ea.DenseCausal(t["q"], t["k"], t["v"], causal=True, scale=cfg.scale)
+    drv.step(t["do"])
+    torch.cuda.synchronize()
+    return t, drv
+
+
+def _sampled_rows(S, rng, n=24):
+    """Tile-boundary rows, the first and last rows, and random rows."""
+    picks = {0, 1, 31, 32, 63, 64, 127, 128, S // 2, S - 129, S - 128, S - 2, S - 1}
+    picks |= set(rng.integers(0, S, size=n).tolist())
+    return np.array(sorted(p for p in picks if 0 <= p < S))
+
+
+def _check_rows(name, t, drv, h, rows, pos_q, pos_k, scale):
+    q, k, v, do = (_head_np(t[n], h) for n in ("q", "k", "v", "do"))
+    ref = oracle.attn_bwd(q[rows], k, v, do[rows], pos_q[rows], pos_k, True, scale)
+    assert_close(f"{name} h{h} O(rows)", _head_np(drv.o, h)[rows], ref["o"])
+    assert_lse(f"{name} h{h} LSE(rows)", _head_np(drv.lse, h)[rows], ref["lse"])
+    assert_close(f"{name} h{h} dQ(rows)", _head_np(drv.dq, h)[rows], ref["dq"])
+
+
+def _check_tail_keys(name, t, drv, h, pos_q, pos_k, scale, n_keys=256):
+    """The visible keys with the largest positions: all their queries fit in one oracle call."""
+    visible = np.nonzero(pos_k <= pos_q.max())[0]
+    keys = np.sort(visible[np.argsort(pos_k[visible])[-n_keys:]])
+    kmin = pos_k[keys].min()
+    qrows = np.nonzero(pos_q >= kmin)[0]
+    q, k, v, do = (_head_np(t[n], h) for n in ("q", "k", "v", "do"))
+    ref = oracle.attn_bwd(q[qrows], k, v, do[qrows], pos_q[qrows], pos_k, True, scale)
+    assert_close(f"{name} h{h} dK(tail keys)", _head_np(drv.dk, h)[keys], ref["dk"][keys])
+    assert_close(f"{name} h{h} dV(tail keys)", _head_np(drv.dv, h)[keys], ref["dv"][keys])
+
+
+def _check_properties(name, t, drv, pos_q, pos_k):
+    # keys that no query may see
+    dead = pos_k > pos_q.max()
+    if dead.any():
+        idx = torch.from_numpy(np.nonzero(dead)[0]).to(DEV)
+        assert float(drv.dk[0, idx].abs().max()) == 0.0 and float(drv.dv[0, idx].abs().max()) == 0.0
+    # sum over keys of dK vanishes; sum over keys of dV equals the sum of dO (every row has keys here)
+    f64 = torch.float64
+    sk = drv.dk[0].sum(dim=0, dtype=f64)                      # [H, D]
+    ak = drv.dk[0].abs().sum(dim=0, dtype=f64).clamp_min(1e-30)
+    sv = drv.dv[0].sum(dim=0, dtype=f64)
+    sd = t["do"][0].sum(dim=0, dtype=f64)
+    ratio = float((sk.abs() / ak).max())
+    print(f"  {name}: max |sum_j dK_j| / sum_j |dK_j| = {ratio:.2e}", flush=True)
+    assert ratio < 1e-2, f"{name}: sum_j dK_j far from 0"
+    rel = float((sv - sd).norm() / sd.norm())
+    print(f"  {name}: |sum dV - sum dO| / |sum dO| = {rel:.2e}", flush=True)
+    assert rel < 5e-3
+
+
+@pytest.mark.timeout(900)
+def test_c2_full_heads():
+    cfg = synth.get("c2")
+    banner(cfg.name)
+    t, drv = _run_dense(cfg)
+    pos = np.arange(cfg.S)
+    heads = [0, cfg.H - 1, int(np.random.default_rng(cfg.seed).integers(1, cfg.H - 1))]
+    ref = oracle.attn_bwd_heads(t["q"], t["k"], t["v"], t["do"], pos, pos, True, cfg.scale, heads=heads)
+    got = {n: getattr(drv, n)[:, :, heads] for n in ("o", "lse", "dq", "dk", "dv")}
+    assert_close("O", got["o"], ref["o"])
+    assert_lse("LSE", got["lse"], ref["lse"])
+    assert_close("dQ", got["dq"], ref["dq"])
+    assert_close("dK", got["dk"], ref["dk"])
+    assert_close("dV", got["dv"], ref["dv"])
+    _check_properties(cfg.name, t, drv, pos, pos)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", ["t", "c5"])
+def test_dense_sampled(key):
+    cfg = synth.get(key)
+    banner(cfg.name)
+    t, drv = _run_dense(cfg)
+    pos = np.arange(cfg.S)
+    rng = np.random.default_rng(cfg.seed)
+    for h in (0, cfg.H - 1):
+        _check_rows(cfg.name, t, drv, h, _sampled_rows(cfg.S, rng), pos, pos, cfg.scale)
+        _check_tail_keys(cfg.name, t, drv, h, pos, pos, cfg.scale)
+    _check_properties(cfg.name, t, drv, pos, pos)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", ["c3", "c4"])
+def test_ring_sampled(key):
+    cfg = synth.get(key)
+    banner(cfg.name)
+    t = synth.make_ring_case(cfg, DEV)
+    drv = ea.ZigzagRingRank(t["q"], t["k"], t["v"], cfg.W, cfg.rank, scale=cfg.scale)
+    drv.step(t["do"])
+    torch.cuda.synchronize()
+    S = cfg.s_total
+    pos_q = oracle.zigzag_positions(S, cfg.W, cfg.rank)
+    pos_k = np.concatenate([oracle.zigzag_positions(S, cfg.W, s) for s in range(cfg.W)])
+    rng = np.random.default_rng(cfg.seed)
+    C = cfg.C
+    rows = np.array(sorted({0, 1, C - 1, C, C + 1, 2 * C - 1} | set(rng.integers(0, 2 * C, size=24).tolist())))
+    for h in (0, cfg.H - 1):
+        _check_rows(cfg.name, t, drv, h, rows, pos_q, pos_k, cfg.scale)
+        # keys just below the rank's last query position: few queries see them
+        _check_tail_keys(cfg.name, t, drv, h, pos_q, pos_k, cfg.scale)
+    _check_properties(cfg.name, t, drv, pos_q, pos_k)

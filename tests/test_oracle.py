@@ -360,3 +360,27 @@ def test_zigzag_rejects_bad_layout():
         oracle.zigzag_positions(10, 3, 0)
     with pytest.raises(ValueError):
         oracle.zigzag_positions(8, 2, 2)
+
+
+# ---------------------------------------------------------------- allowed-pair sums (probe expectations)
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_allowed_sums_match_mask(causal):
+    rng = np.random.default_rng(41)
+    for _ in range(5):
+        sq, sk = int(rng.integers(1, 60)), int(rng.integers(1, 80))
+        pq = rng.integers(0, 50, size=sq)
+        pk = rng.integers(0, 50, size=sk)
+        w = rng.integers(0, 3, size=(sk, 4))
+        ref = A.allowed_mask(pq, pk, causal).astype(np.int64) @ w
+        assert np.array_equal(A.allowed_sums(pq, pk, causal, w), ref)
+
+
+def test_allowed_sums_zigzag_count():
+    # every rank of an 8-rank zigzag layout sees 16 C^2 + C causal pairs
+    C, W = 11, 8
+    S = 2 * W * C
+    pk = np.arange(S)
+    for r in range(W):
+        pq = oracle.zigzag_positions(S, W, r)
+        assert A.allowed_sums(pq, pk, True, np.ones((S, 1))).sum() == 16 * C * C + C

@@ -27,6 +27,8 @@ MUTANTS = {
     "merge_swapped": ("w1 * o1 + w2 * o2", "w2 * o1 + w1 * o2"),
     "merge_no_log": ("lse = np.logaddexp(lse1, lse2)", "lse = np.maximum(lse1, lse2)"),
     "pv_transposed_v": ("o = p @ vc", "o = p @ vc[::-1]"),
+    "sums_strict": ('side="right"', 'side="left"'),
+    "sums_unsorted": ("csum[n]", "csum[np.minimum(n + 1, len(csum) - 1)]"),
 }
 
 ZMUTANTS = {
@@ -43,6 +45,7 @@ PINS = [
     lambda: T.test_torch_autograd(0, True, 4),
     T.test_zero_query_counts_and_means,
     lambda: T.test_split_merge_equals_unsplit("random", True),
+    lambda: T.test_allowed_sums_match_mask(True),
 ]
 
 ZPINS = [
@@ -72,7 +75,7 @@ def _fails(pins):
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_attention_mutant_is_caught(name, monkeypatch):
     mod = _load_mutant(A, *MUTANTS[name])
-    for fn in ("allowed_mask", "attn_fwd", "attn_bwd", "lse_merge", "_block_fwd"):
+    for fn in ("allowed_mask", "allowed_sums", "attn_fwd", "attn_bwd", "lse_merge", "_block_fwd"):
         monkeypatch.setattr(A, fn, getattr(mod, fn))
     with np.errstate(all="ignore"):
         assert _fails(PINS) >= 1, f"no pin caught mutant {name}"
