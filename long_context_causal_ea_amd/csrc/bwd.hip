@@ -4,14 +4,15 @@
 //
 // Three launches on one stream:
 //  1. delta:  Delta_i = <dO_i, O_i>, one pass over O and dO (HBM-bound).
-//  2. dkdv:   one workgroup per 128-key block (4 waves x 32 keys).  Each wave
-//             keeps its keys' K and V rows in registers and its dK^T, dV^T
-//             accumulators in fp32 registers, and streams 32-row query tiles
-//             (Q, dO, LSE, Delta) through double-buffered LDS.  Scores are
-//             computed with the key on the MFMA column (lane) axis, so P and dS
-//             come out of the MFMA already in the B-operand form that
-//             dV^T += dO^T P and dK^T += Q^T dS need; the dO^T and Q^T operands
-//             are read from the row-major tiles with the LDS transpose read.
+//  2. dkdv:   one workgroup per block of 16*NW keys (NW waves x 16 keys).  Each
+//             wave keeps its keys' K and V rows in registers and its dK^T, dV^T
+//             accumulators in fp32 registers, and streams query tiles (Q, dO,
+//             LSE, Delta) through double-buffered LDS.  Scores are computed
+//             with the key on the MFMA column (lane) axis of the 16x16x32 MFMA,
+//             so P and dS come out of the MFMA already in the B-operand form
+//             that dV^T += dO^T P and dK^T += Q^T dS need; the dO^T and Q^T
+//             operands are read from the row-major tiles with the LDS
+//             transpose read.
 //  3. dq:     one workgroup per 128-query block, streaming key tiles like the
 //             forward; recomputes S^T and dP^T with the query on the lane axis
 //             and accumulates dQ^T += K^T dS^T in registers (K^T by transpose
