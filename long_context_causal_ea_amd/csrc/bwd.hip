@@ -4,11 +4,11 @@
 //
 // Three launches on one stream:
 //  1. delta:  Delta_i = <dO_i, O_i>, one pass over O and dO (HBM-bound).
-//  2. dkdv:   one workgroup per block of 16*NW keys (NW waves x 16 keys).  Each
-//             wave keeps its keys' K and V rows in registers and its dK^T, dV^T
-//             accumulators in fp32 registers, and streams query tiles (Q, dO,
-//             LSE, Delta) through double-buffered LDS.  Scores are computed
-//             with the key on the MFMA column (lane) axis of the 16x16x32 MFMA,
+//  2. dkdv:   one workgroup per 128-key block (4 waves x 32 keys, one wave per
+//             SIMD).  Each wave keeps its keys' K and V rows in registers and
+//             its dK^T, dV^T accumulators in fp32 registers, and streams 32-row
+//             query tiles (Q, dO, LSE, Delta) through a direct-to-LDS ring.
+//             Scores are computed with the key on the MFMA column (lane) axis,
 //             so P and dS come out of the MFMA already in the B-operand form
 //             that dV^T += dO^T P and dK^T += Q^T dS need; the dO^T and Q^T
 //             operands are read from the row-major tiles with the LDS
@@ -30,12 +30,6 @@
 #endif
 #ifndef EA_DQ_MIN_WG
 #define EA_DQ_MIN_WG 2
-#endif
-#ifndef EA_DKDV_WAVES
-#define EA_DKDV_WAVES 8  // waves per dK/dV workgroup (16 keys each); 4 or 8
-#endif
-#ifndef EA_DKDV_BQ
-#define EA_DKDV_BQ 64  // query rows per dK/dV tile; 32 or 64
 #endif
 
 namespace ea {
@@ -100,34 +94,44 @@ __device__ __forceinline__ float lse_to_log2(float l) {
 }
 
 // ------------------------------------------------------------------ dK, dV
-// One workgroup per block of NW*16 keys; each wave owns 16 keys.  The 16x16x32
-// MFMA puts the wave's 16 keys on the lane axis, so P and dS leave the score
-// products as B operands of dV^T += dO^T P and dK^T += Q^T dS, and the dK^T /
-// dV^T accumulators of 16 keys x D dims take D/2 registers each: two waves fit
-// per SIMD.
+// One workgroup = 4 waves = 128 keys of one (batch, head); each wave owns 32
+// keys, one wave per SIMD with the whole register file.  The wave keeps its
+// keys' K and V rows as B operands of the 32x32x16 MFMA (key on the lane axis)
+// and its dK^T, dV^T accumulators (32 keys x D, fp32) in registers.
+//
+// 32-row query tiles (Q, dO, and the LSE / Delta of those rows) stream through a
+// 4-stage LDS ring filled by direct global->LDS loads, three tiles in flight.
+// Per tile:  S = Q K^T and dP = dO V^T (query on the MFMA row axis; each lane
+// holds 16 queries of one key), P = exp2(S*c - LSE*log2 e), dS = P (dP - Delta),
+// then dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read from the
+// row-major tiles by the LDS transpose read and P, dS packed to bf16 straight
+// from the score registers as B operands.  The loop is software-pipelined like
+// the forward: the score products of tile t+1 go to the matrix cores while the
+// vector ALUs turn the scores of tile t into P and dS.
 template <int D>
 struct DkdvCfg {
-  static constexpr int NW = EA_DKDV_WAVES, NT = 64 * NW, BKV = 16 * NW, BQ = EA_DKDV_BQ;
-  static constexpr int NQB = BQ / 16, NKK = BQ / 32;  // 16-query score blocks, 32-query reduction steps
-  static constexpr int CPR = D / 8;
-  static constexpr int NL = 2 * BQ * CPR / NT;  // 16-byte chunks per thread per tile (Q and dO together)
+  static constexpr int NW = 4, NT = 256, BKV = 32 * NW, BQ = 32, NST = 4;
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;            // rows one wave covers per direct-to-LDS load
+  static constexpr int NQL = BQ / (NW * RPI);     // direct-to-LDS loads per thread per tile, per tensor
   static constexpr int LDS_T = BQ * D;
-  static_assert(NL * NT == 2 * BQ * CPR && NL >= 1 && BQ % 32 == 0 && 2 * BQ <= NT, "unsupported query tile");
+  static_assert(NQL >= 1 && NQL * NW * RPI == BQ, "unsupported query tile");
 };
 
 template <int D>
-__global__ __launch_bounds__(64 * EA_DKDV_WAVES, 8 / EA_DKDV_WAVES) void dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   using Cfg = DkdvCfg<D>;
-  constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, CPR = Cfg::CPR, NT = Cfg::NT;
-  constexpr int NKS = D / 32, NDB = D / 16, NQB = Cfg::NQB, NKK = Cfg::NKK;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][Cfg::LDS_T];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[2][Cfg::LDS_T];   // dO
-  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+  constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, CPR = Cfg::CPR, NST = Cfg::NST, RPI = Cfg::RPI;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  // stage s: Q tile at QO[s][0], dO tile at QO[s][LDS_T] (one array, so that the
+  // two operands of a step differ by an immediate offset)
+  __shared__ __attribute__((aligned(16))) uint16_t QO[NST][2 * Cfg::LDS_T];
+  __shared__ __attribute__((aligned(16))) float Ss[NST][2 * BQ];  // LSE of the rows, then Delta
+  constexpr int OT = Cfg::LDS_T;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
-  const int l16 = lane & 15, g4 = lane >> 4;
+  const int ln = lane & 31, g = lane >> 5;
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = work / p.nblk;
@@ -143,21 +147,24 @@ __global__ __launch_bounds__(64 * EA_DKDV_WAVES, 8 / EA_DKDV_WAVES) void dkdv_ke
   const float* delp = p.delta + b * p.row_bstride + h;
 
   const int j0 = kb * BKV;
-  const int kw0 = j0 + 16 * w;
-  const int krow = kw0 + l16;
+  const int kw0 = j0 + 32 * w;
+  const int krow = kw0 + ln;
   const bool key_ok = krow < p.Sk;
 
-  // this lane's key row in MFMA B-operand form (8 dims per lane per 32-dim step)
+  // this lane's key row as MFMA B operand: dims 16*ks + 8*g .. +7
   bf16x8 kf[NKS], vf[NKS];
   {
-    const long off = (long)(key_ok ? krow : 0) * p.rs + 8 * g4;
+    const long off = (long)(key_ok ? krow : 0) * p.rs + 8 * g;
     const u32x4* ksrc = reinterpret_cast<const u32x4*>(kp + off);
     const u32x4* vsrc = reinterpret_cast<const u32x4*>(vp + off);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = as_bf16x8(key_ok ? ksrc[4 * ks] : u32x4{0u, 0u, 0u, 0u});
-      vf[ks] = as_bf16x8(key_ok ? vsrc[4 * ks] : u32x4{0u, 0u, 0u, 0u});
+      kf[ks] = as_bf16x8(key_ok ? ksrc[2 * ks] : u32x4{0u, 0u, 0u, 0u});
+      vf[ks] = as_bf16x8(key_ok ? vsrc[2 * ks] : u32x4{0u, 0u, 0u, 0u});
     }
+    // land these before the direct-to-LDS ring starts (see the forward kernel)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
   }
   const int kpos = seg_pos(p.ks, key_ok ? krow : (p.Sk - 1));
   QueryWindow qwin = query_window(p.qs, kpos, p.causal);
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(64 * EA_DKDV_WAVES, 8 / EA_DKDV_WAVES) void dkdv_ke
   const int wg_end = min(j0 + BKV, p.Sk);
   int kmin_wg, kmax_wg;
   seg_range(p.ks, j0, wg_end, kmin_wg, kmax_wg);
-  const int kw1 = min(kw0 + 16, p.Sk);
+  const int kw1 = min(kw0 + 32, p.Sk);
   const bool wave_live = kw0 < kw1;
   int kmin_w = 0x7fffffff, kmax_w = 0;
   if (wave_live) seg_range(p.ks, kw0, kw1, kmin_w, kmax_w);
@@ -195,155 +202,201 @@ __global__ __launch_bounds__(64 * EA_DKDV_WAVES, 8 / EA_DKDV_WAVES) void dkdv_ke
   const int nt = nA + nC;
   auto tile_of = [&](int t) { return t < nA ? tA0 + t : tC0 + (t - nA); };
 
-  f32x4 dka[NDB], dva[NDB];
+  f32x16 dka[NDB], dva[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    dka[db] = f32x4{};
-    dva[db] = f32x4{};
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
   }
 
-  // staging: chunk c of the tile pair (Q rows then dO rows); consecutive threads
-  // take consecutive 16-byte chunks of a row
-  u32x4 sreg[Cfg::NL];
-  float lreg = 0.f;
-
-  auto load_tile = [&](int it) {
-    const int i0 = it * BQ;
+  // ---- direct global -> LDS loads (lane i fills 16-byte slot i % CPR of row
+  // i / CPR, i.e. chunk slot ^ swz(row) of that row); wave 0 also moves the 32
+  // LSE and 32 Delta values of the tile (4 bytes per lane).
+  const int dma_row = lane / CPR, dma_slot = lane % CPR;
+  uint32_t dma_off[Cfg::NQL];  // byte offset of this lane's 16 bytes within a tile whose first row is 0
 #pragma unroll
-    for (int k = 0; k < Cfg::NL; ++k) {
-      const int c = tid + NT * k;
-      const int tns = c / (BQ * CPR), within = c % (BQ * CPR);
-      const int row = within / CPR, col = within % CPR;
-      const int i = i0 + row;
-      const uint16_t* src = tns ? op : qp;
-      sreg[k] = i < p.Sq ? *reinterpret_cast<const u32x4*>(src + (long)i * p.rs + col * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < 2 * BQ) {
-      const int i = i0 + (tid % BQ);
-      if (tid < BQ)
-        lreg = i < p.Sq ? lse_to_log2(lsep[(long)i * p.H]) : __builtin_inff();
-      else
-        lreg = i < p.Sq ? delp[(long)i * p.H] : 0.f;
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int it = 0; it < Cfg::NQL; ++it) {
+    const int row = RPI * (w + 4 * it) + dma_row;
+    dma_off[it] = (uint32_t)(((long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
+  }
+  const float* stat_src = g == 0 ? lsep : delp;  // per lane: LSE (lanes 0..31) or Delta (32..63)
+  auto issue_tile = [&](auto STAGE, int t) {
+    constexpr int stage = decltype(STAGE)::value;
+    const int tt = t < nt ? t : nt - 1;  // past the end: reload the last tile into a stage nobody reads
+    const int i0 = __builtin_amdgcn_readfirstlane(tile_of(tt) * BQ);
+    const bool whole = i0 + BQ <= p.Sq;
+    const uint16_t* qt = qp + (long)i0 * p.rs;
+    const uint16_t* ot = op + (long)i0 * p.rs;
 #pragma unroll
-    for (int k = 0; k < Cfg::NL; ++k) {
-      const int c = tid + NT * k;
-      const int tns = c / (BQ * CPR), within = c % (BQ * CPR);
-      uint16_t* dst = tns ? Os[buf] : Qs[buf];
-      *reinterpret_cast<u32x4*>(&dst[tile_off<D>(within / CPR, within % CPR)]) = sreg[k];
-    }
-    if (tid < BQ)
-      Ls[buf][tid] = lreg;
-    else if (tid < 2 * BQ)
-      Ds[buf][tid - BQ] = lreg;
-  };
-
-  const int swq = swz<D>(l16);                 // Q/dO operand rows are 16*mb + l16
-  const int trow = 4 * g4 + (l16 >> 2);        // transpose read: query row (+16 for the second half)
-  const int tcol = 4 * (l16 & 3);              // transpose read: dim column within 16
-
-  if (nt > 0) load_tile(tile_of(0));
-
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    const int it = tile_of(t);
-    const int i0 = it * BQ;
-    store_tile(buf);
-    __syncthreads();
-    if (t + 1 < nt) load_tile(tile_of(t + 1));
-
-    int cls = kSkip;
-    if (wave_live) {
-      const int iend = min(i0 + BQ, p.Sq);
-      int qmn, qmx;
-      seg_range(p.qs, i0, iend, qmn, qmx);
-      const bool tail = (i0 + BQ > p.Sq) || (kw0 + 16 > p.Sk);
-      if (!p.causal) cls = tail ? kPartial : kFull;
-      else if (kmin_w > qmx) cls = kSkip;
-      else if (kmax_w <= qmn && !tail) cls = kFull;
-      else cls = kPartial;
-    }
-    if (cls == kSkip) continue;
-
-    // S = Q K^T and dP = dO V^T for 16-query blocks; lane = key,
-    // register e of block mb = query 16*mb + 4*g4 + e
-    f32x4 s[NQB], dp[NQB];
-#pragma unroll
-    for (int mb = 0; mb < NQB; ++mb) {
-      s[mb] = f32x4{};
-      dp[mb] = f32x4{};
-      const uint16_t* qrow = &Qs[buf][(16 * mb + l16) * D];
-      const uint16_t* orow = &Os[buf][(16 * mb + l16) * D];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int o = ((4 * ks + g4) ^ swq) << 3;
-        const u32x4 aq = *reinterpret_cast<const u32x4*>(qrow + o);
-        s[mb] = mfma16(as_bf16x8(aq), kf[ks], s[mb]);
-        const u32x4 ao = *reinterpret_cast<const u32x4*>(orow + o);
-        dp[mb] = mfma16(as_bf16x8(ao), vf[ks], dp[mb]);
+    for (int it = 0; it < Cfg::NQL; ++it) {
+      const int row0 = RPI * (w + 4 * it);
+      uint32_t off = dma_off[it];
+      if (!whole) {  // rows past the end load the last row; the element mask removes them
+        const int row = row0 + dma_row;
+        const int i = min(row, p.Sq - 1 - i0);
+        off = (uint32_t)(((long)i * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
       }
+      dma16_s(qt, off, &QO[stage][row0 * D]);
+      dma16_s(ot, off, &QO[stage][OT + row0 * D]);
     }
+    if (w == 0) dma4(stat_src + (long)min(i0 + ln, p.Sq - 1) * p.H, &Ss[stage][0]);
+  };
+  constexpr int LOADS = 2 * Cfg::NQL;  // per tile, waves 1..3 (wave 0: one more)
 
-    float pv[NQB][4], dsv[NQB][4];
+  // per-lane LDS offsets (elements)
+  // Q / dO operand of the scores: row ln, chunk 2*ks+g = slot 2*(ks ^ qx) + (g ^ (swz & 1))
+  const int qx = swz<D>(ln) >> 1, qbase = ln * D + ((g ^ (swz<D>(ln) & 1)) << 3);
+  int tofs[2][NDB];  // dO^T / Q^T transpose read: rows 8*half + trow (+16 per k-step), 32 dims per block
+  {
+    const int trow = 4 * g + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-    for (int mb = 0; mb < NQB; ++mb) {
-      const int qi = 16 * mb + 4 * g4;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][qi]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][qi]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = fast_exp2(__builtin_fmaf(s[mb][e], p.c, -l4[e]));
-        if (cls == kPartial) x = in_window(qwin, i0 + qi + e) ? x : 0.f;
-        pv[mb][e] = x;
-        dsv[mb][e] = x * (dp[mb][e] - d4[e]);
-      }
-    }
-
-    // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over 32 queries per step:
-    // query blocks 2*kk and 2*kk+1; dO^T and Q^T read transposed from the
-    // row-major tiles)
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int m0 = 2 * kk, m1 = 2 * kk + 1;
-      const bf16x8 pb = pack_bf16x8(pv[m0][0], pv[m0][1], pv[m0][2], pv[m0][3], pv[m1][0], pv[m1][1], pv[m1][2],
-                                    pv[m1][3]);
-      const bf16x8 sb = pack_bf16x8(dsv[m0][0], dsv[m0][1], dsv[m0][2], dsv[m0][3], dsv[m1][0], dsv[m1][1],
-                                    dsv[m1][2], dsv[m1][3]);
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int col = 16 * db + tcol;
-        const int o0 = tile_off<D>(32 * kk + trow, col >> 3) + (col & 7);
-        const int o1 = tile_off<D>(32 * kk + 16 + trow, col >> 3) + (col & 7);
-        const u32x2 olo = ds_read_tr16(&Os[buf][o0]);
-        const u32x2 ohi = ds_read_tr16(&Os[buf][o1]);
-        const u32x4 ao = {olo[0], olo[1], ohi[0], ohi[1]};
-        dva[db] = mfma16(as_bf16x8(ao), pb, dva[db]);
-        const u32x2 qlo = ds_read_tr16(&Qs[buf][o0]);
-        const u32x2 qhi = ds_read_tr16(&Qs[buf][o1]);
-        const u32x4 aq = {qlo[0], qlo[1], qhi[0], qhi[1]};
-        dka[db] = mfma16(as_bf16x8(aq), sb, dka[db]);
+        const int col = 32 * db + tcol;
+        tofs[half][db] = tile_off<D>(8 * half + trow, col >> 3) + (col & 7);
+      }
+  }
+
+  // wave-level class of tile t: FULL (no mask) or PARTIAL (element mask).  A
+  // tile without any allowed pair for this wave is computed fully masked, which
+  // keeps the loop one straight pipeline.
+  auto classify = [&](int t) {
+    const int i0 = tile_of(t) * BQ;
+    if (!wave_live || i0 + BQ > p.Sq || kw0 + 32 > p.Sk) return (int)kPartial;
+    if (!p.causal) return (int)kFull;
+    int qmn, qmx;
+    seg_range(p.qs, i0, i0 + BQ, qmn, qmx);
+    return kmax_w <= qmn ? (int)kFull : (int)kPartial;
+  };
+
+  // one k-step of S = Q K^T and dP = dO V^T for the tile in stage STAGE; output
+  // register r of lane l holds query 8*(r/4) + 4*g + r%4 of key ln
+  auto score_k = [&](auto STAGE, int ks, f32x16& s, f32x16& dp) {
+    constexpr int stage = decltype(STAGE)::value;
+    const int o = qbase + ((ks ^ qx) << 4);
+    const u32x4 aq = *reinterpret_cast<const u32x4*>(&QO[stage][o]);
+    const u32x4 ao = *reinterpret_cast<const u32x4*>(&QO[stage][OT + o]);
+    s = mfma32(as_bf16x8(aq), kf[ks], ks == 0 ? f32x16{} : s);
+    dp = mfma32(as_bf16x8(ao), vf[ks], ks == 0 ? f32x16{} : dp);
+  };
+  auto scores = [&](auto STAGE, f32x16& s, f32x16& dp) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) score_k(STAGE, ks, s, dp);
+  };
+
+  auto wait_ring = [&](auto N) {  // this wave's loads of tile t+1 have landed, then barrier
+    constexpr int n = decltype(N)::value;
+    if (w == 0)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n * (LOADS + 1)) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n * LOADS) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  const float c = p.c;
+  constexpr float NEG_INF = -__builtin_inff();
+
+  // one pipeline step: P, dS and the dV/dK products of tile t (scores in
+  // s_cur/dp_cur, stage STAGE) interleaved with the score products of tile t+1
+  auto step = [&](auto STAGE, int t, f32x16& s_cur, f32x16& dp_cur, int& cls_cur, f32x16& s_nx, f32x16& dp_nx,
+                  int& cls_nx) {
+    constexpr int stage = decltype(STAGE)::value;
+    constexpr int nstage = (stage + 1) % NST, fstage = (stage + NST - 1) % NST;
+    wait_ring(std::integral_constant<int, NST - 3>{});
+    issue_tile(std::integral_constant<int, fstage>{}, t + NST - 1);
+    const int i0 = tile_of(t) * BQ;
+    cls_nx = t + 1 < nt ? classify(t + 1) : (int)kFull;
+
+    // element mask of a partial tile: masked scores become -inf (probability 0)
+    if (cls_cur == kPartial) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        s_cur[r] = in_window(qwin, i) ? s_cur[r] : NEG_INF;
       }
     }
+
+    // One straight-line block: the score products of tile t+1 (matrix cores)
+    // interleave with P and dS of tile t (vector ALUs).  The LSE enters as
+    // -LSE*log2(e), clamped so that a row without any allowed key (LSE = -inf)
+    // still gives exp2(-inf) = 0 on its (masked) scores.
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      score_k(std::integral_constant<int, nstage>{}, ks, s_nx, dp_nx);
+#pragma unroll
+      for (int u = 0; u < 16 / NKS; ++u) {
+        const int r = (16 / NKS) * ks + u;
+        const int qi = 8 * (r >> 2) + 4 * g + (r & 3);
+        const float nl = fminf(Ss[stage][qi] * -kLog2e, 3.0e38f);
+        const float x = fast_exp2(__builtin_fmaf(s_cur[r], c, nl));
+        pv[r] = x;
+        dsv[r] = x * (dp_cur[r] - Ss[stage][BQ + qi]);
+      }
+    }
+    // dV^T += dO^T P ; dK^T += Q^T dS over two 16-query k-steps
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int o = 8 * kk;
+      const bf16x8 pb = pack_bf16x8(pv[o], pv[o + 1], pv[o + 2], pv[o + 3], pv[o + 4], pv[o + 5], pv[o + 6], pv[o + 7]);
+      const bf16x8 sb =
+          pack_bf16x8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5], dsv[o + 6], dsv[o + 7]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2 olo = ds_read_tr16(&QO[stage][OT + tofs[0][db] + 16 * kk * D]);
+        const u32x2 ohi = ds_read_tr16(&QO[stage][OT + tofs[1][db] + 16 * kk * D]);
+        const u32x4 ao = {olo[0], olo[1], ohi[0], ohi[1]};
+        dva[db] = mfma32(as_bf16x8(ao), pb, dva[db]);
+        const u32x2 qlo = ds_read_tr16(&QO[stage][tofs[0][db] + 16 * kk * D]);
+        const u32x2 qhi = ds_read_tr16(&QO[stage][tofs[1][db] + 16 * kk * D]);
+        const u32x4 aq = {qlo[0], qlo[1], qhi[0], qhi[1]};
+        dka[db] = mfma32(as_bf16x8(aq), sb, dka[db]);
+      }
+    }
+  };
+
+  if (nt > 0) {
+    static_assert(NST == 4, "the loop below is unrolled for a ring of 4 stages");
+    issue_tile(std::integral_constant<int, 0>{}, 0);
+    issue_tile(std::integral_constant<int, 1>{}, 1);
+    issue_tile(std::integral_constant<int, 2>{}, 2);
+    wait_ring(std::integral_constant<int, NST - 2>{});
+    int cls_a = classify(0), cls_b = kFull;
+    f32x16 s_a, dp_a, s_b, dp_b;
+    scores(std::integral_constant<int, 0>{}, s_a, dp_a);
+    for (int t = 0; t < nt; t += 4) {
+      step(std::integral_constant<int, 0>{}, t, s_a, dp_a, cls_a, s_b, dp_b, cls_b);
+      if (t + 1 >= nt) break;
+      step(std::integral_constant<int, 1>{}, t + 1, s_b, dp_b, cls_b, s_a, dp_a, cls_a);
+      if (t + 2 >= nt) break;
+      step(std::integral_constant<int, 2>{}, t + 2, s_a, dp_a, cls_a, s_b, dp_b, cls_b);
+      if (t + 3 >= nt) break;
+      step(std::integral_constant<int, 3>{}, t + 3, s_b, dp_b, cls_b, s_a, dp_a, cls_a);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // retire the trailing (unused) loads
   }
 
   if (!key_ok || nt == 0) return;
   float* dkp = p.dk + b * p.k_bstride + (long)h * D_ + (long)krow * p.rs;
   float* dvp = p.dv + b * p.k_bstride + (long)h * D_ + (long)krow * p.rs;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int d0 = 16 * db + 4 * g4;
-    f32x4 k4 = *reinterpret_cast<f32x4*>(dkp + d0);
-    f32x4 v4 = *reinterpret_cast<f32x4*>(dvp + d0);
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      k4[e] += p.scale * dka[db][e];
-      v4[e] += dva[db][e];
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * db + 8 * q4 + 4 * g;
+      f32x4 k4 = *reinterpret_cast<f32x4*>(dkp + d0);
+      f32x4 v4 = *reinterpret_cast<f32x4*>(dvp + d0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k4[e] += p.scale * dka[db][4 * q4 + e];
+        v4[e] += dva[db][4 * q4 + e];
+      }
+      *reinterpret_cast<f32x4*>(dkp + d0) = k4;
+      *reinterpret_cast<f32x4*>(dvp + d0) = v4;
     }
-    *reinterpret_cast<f32x4*>(dkp + d0) = k4;
-    *reinterpret_cast<f32x4*>(dvp + d0) = v4;
-  }
 }
 
 // ------------------------------------------------------------------ dQ

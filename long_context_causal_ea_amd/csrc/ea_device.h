@@ -58,19 +58,26 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float x0, float x1, float x2, floa
 
 // ---- LDS tiles: row-major [rows][D] bf16, 16-byte chunks XOR-swizzled per row.
 // Chunk c of row r is stored at chunk slot c ^ swz(r).  The swizzle keeps the
-// access patterns of the kernels free of bank conflicts on 64 banks x 4 bytes:
-// (a) 16 lanes reading the same chunk of 16 consecutive rows (MFMA operands
-// whose reduction index runs along D), (b) transpose reads (below) where 32
-// lanes read 4 consecutive rows x 64 bytes (32x32 MFMA operands) and (c) where
-// 32 lanes read 8 consecutive rows x 32 bytes (16x16 MFMA operands).  For 16
-// chunks per row that asks for a permutation of the row's low 4 bits whose top
-// 2 bits differ across any aligned 4 rows and top 3 bits across any aligned 8
-// rows: the 3-bit reversal of r mod 8, then bit 3 of r.
+// access patterns of the kernels free of bank conflicts on 64 banks x 4 bytes.
+// Measured on gfx950: a 16-byte read is served in four passes, each taking
+// lanes 8j..8j+7 together with lanes 32+8j..32+8j+7; a transpose read in two
+// passes of 32 consecutive lanes; a 16-byte write in passes of 16 consecutive
+// lanes.  The patterns are
+//  (a) 32x32x16 operands: lanes l and l+32 read chunks 2k and 2k+1 of row l%32,
+//  (b) 16x16x32 operands: lanes l, l+16, l+32, l+48 read chunks 4k..4k+3 of
+//      row l%16, so one pass holds chunks 4k and 4k+2 of 8 consecutive rows,
+//  (c) transpose reads of 4 consecutive rows x 64 bytes (32x32 operands) or of
+//      8 consecutive rows x 32 bytes (16x16 operands) per 32 lanes,
+//  (d) row-wise tile writes.
+// For 16 chunks per row they are all conflict-free when, over every aligned 8
+// rows, bits {1,2,3} and bits {0,2,3} of swz(r) both take 8 distinct values,
+// and over every aligned 4 rows bits {2,3} take 4 distinct values:
+// swz(r) = (r mod 4) * 4 + (3 if bit 2 of r else 0) ^ (bit 3 of r).
 template <int D>
 __device__ __forceinline__ int swz(int r);
 template <>
 __device__ __forceinline__ int swz<128>(int r) {  // 16 chunks per row
-  return ((r & 1) << 3) | (r & 2) << 1 | ((r >> 2) & 1) << 1 | ((r >> 3) & 1);
+  return ((r & 3) << 2) | ((((r >> 2) & 1) * 3) ^ ((r >> 3) & 1));
 }
 template <>
 __device__ __forceinline__ int swz<64>(int r) {  // 8 chunks per row, two rows per 256 bytes
@@ -101,6 +108,21 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
 __device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
   const uint32_t m0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)lds_base);
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
+}
+
+// The same with a uniform 64-bit base held in scalar registers and a 32-bit
+// per-lane byte offset (one vector register per address instead of two).
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const void* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)lds_base);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
+// Direct global -> LDS load of 4 bytes per lane (global_load_lds_dword): lane
+// i's value lands at LDS byte address lds_base + 4*i.  Same ordering rules as
+// dma16.
+__device__ __forceinline__ void dma4(const void* gptr, const void* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)lds_base);
+  asm volatile("global_load_lds_dword %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
 }
 
 // Wait until at most N direct-to-LDS loads of this wave are in flight, then
