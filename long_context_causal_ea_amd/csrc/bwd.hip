@@ -21,6 +21,8 @@
 // The dq pass recomputes the two score products instead of exchanging dS
 // through atomics: every output element is then written by exactly one
 // workgroup, without atomics, and results are bitwise reproducible.
+#include <type_traits>
+
 #include "ea_device.h"
 #include "ea_launch.h"
 
@@ -94,43 +96,51 @@ __device__ __forceinline__ float lse_to_log2(float l) {
 }
 
 // ------------------------------------------------------------------ dK, dV
-// One workgroup = 4 waves = 128 keys of one (batch, head); each wave owns 32
-// keys, one wave per SIMD with the whole register file.  The wave keeps its
-// keys' K and V rows as B operands of the 32x32x16 MFMA (key on the lane axis)
-// and its dK^T, dV^T accumulators (32 keys x D, fp32) in registers.
+// One workgroup = 8 waves = 128 keys of one (batch, head), two waves per SIMD.
+// The 32 keys of key group kw (0..3) are shared by a pair of waves:
+//   wave kw     (role A) holds the keys' K rows, computes S = Q K^T, the
+//               probabilities P = exp2(S*c - LSE*log2 e) (element mask on
+//               partial tiles) and dV^T += dO^T P;
+//   wave 4 + kw (role B) holds the V rows, computes dP = dO V^T, takes P of the
+//               same keys from A through LDS, forms dS = P (dP - Delta) and
+//               accumulates dK^T += Q^T dS.
+// Each wave thus needs one operand tensor and one accumulator (32 keys x D fp32)
+// in registers, which leaves room for two waves per SIMD.  Scores use the
+// 32x32x16 MFMA with the key on the lane axis, so P and dS leave the MFMA in
+// the B-operand form of the dV / dK products; dO^T and Q^T are read from the
+// row-major tiles by the LDS transpose read.
 //
-// 32-row query tiles (Q, dO, and the LSE / Delta of those rows) stream through a
-// 4-stage LDS ring filled by direct global->LDS loads, three tiles in flight.
-// Per tile:  S = Q K^T and dP = dO V^T (query on the MFMA row axis; each lane
-// holds 16 queries of one key), P = exp2(S*c - LSE*log2 e), dS = P (dP - Delta),
-// then dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read from the
-// row-major tiles by the LDS transpose read and P, dS packed to bf16 straight
-// from the score registers as B operands.  The loop is software-pipelined like
-// the forward: the score products of tile t+1 go to the matrix cores while the
-// vector ALUs turn the scores of tile t into P and dS.
+// 32-row query tiles (Q, dO, LSE, Delta) stream through a 6-stage LDS ring of
+// direct global->LDS loads (tiles t-1 .. t+1 in use, t+2 .. t+4 in flight).  In step t, A computes the scores of tile t+1 while
+// turning those of tile t into P (software pipeline) and publishes P(t); B
+// computes dP(t) while forming dS(t-1) from P(t-1), published one step earlier,
+// so the one workgroup barrier per step orders both the ring and the exchange.
 template <int D>
 struct DkdvCfg {
-  static constexpr int NW = 4, NT = 256, BKV = 32 * NW, BQ = 32, NST = 4;
-  static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR;            // rows one wave covers per direct-to-LDS load
-  static constexpr int NQL = BQ / (NW * RPI);     // direct-to-LDS loads per thread per tile, per tensor
+  static constexpr int NW = 8, NT = 512, BKV = 128, BQ = 32, NST = 6;
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;               // rows one direct-to-LDS load covers
+  static constexpr int NI = 2 * BQ / RPI;            // loads per tile (Q and dO)
+  static constexpr int NIW = NI / NW;                // loads per wave per tile
   static constexpr int LDS_T = BQ * D;
-  static_assert(NQL >= 1 && NQL * NW * RPI == BQ, "unsupported query tile");
+  static_assert(NIW >= 1 && NIW * NW == NI, "unsupported query tile");
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   using Cfg = DkdvCfg<D>;
   constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, CPR = Cfg::CPR, NST = Cfg::NST, RPI = Cfg::RPI;
   constexpr int NKS = D / 16, NDB = D / 32;
-  // stage s: Q tile at QO[s][0], dO tile at QO[s][LDS_T] (one array, so that the
-  // two operands of a step differ by an immediate offset)
-  __shared__ __attribute__((aligned(16))) uint16_t QO[NST][2 * Cfg::LDS_T];
-  __shared__ __attribute__((aligned(16))) float Ss[NST][2 * BQ];  // LSE of the rows, then Delta
   constexpr int OT = Cfg::LDS_T;
+  // stage s: Q tile at QO[s][0], dO tile at QO[s][OT]
+  __shared__ __attribute__((aligned(16))) uint16_t QO[NST][2 * OT];
+  __shared__ __attribute__((aligned(16))) float Ss[NST][2 * BQ];  // LSE of the rows, then Delta
+  // P of the last two tiles per key group, fp32: [slot][group][r/4][lane][r%4]
+  __shared__ __attribute__((aligned(16))) float Ps[2][4][4][64][4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
+  const int role = w >> 2, kw = w & 3;
   const int ln = lane & 31, g = lane >> 5;
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
@@ -141,43 +151,37 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 
   const uint16_t* qp = p.q + b * p.q_bstride + (long)h * D_;
   const uint16_t* op = p.dout + b * p.q_bstride + (long)h * D_;
-  const uint16_t* kp = p.k + b * p.k_bstride + (long)h * D_;
-  const uint16_t* vp = p.v + b * p.k_bstride + (long)h * D_;
   const float* lsep = p.lse + b * p.row_bstride + h;
   const float* delp = p.delta + b * p.row_bstride + h;
 
   const int j0 = kb * BKV;
-  const int kw0 = j0 + 32 * w;
+  const int kw0 = j0 + 32 * kw;
   const int krow = kw0 + ln;
   const bool key_ok = krow < p.Sk;
 
-  // this lane's key row as MFMA B operand: dims 16*ks + 8*g .. +7
-  bf16x8 kf[NKS], vf[NKS];
+  // this lane's key row of K (role A) or V (role B) as MFMA B operand: dims 16*ks + 8*g .. +7
+  bf16x8 kvf[NKS];
   {
-    const long off = (long)(key_ok ? krow : 0) * p.rs + 8 * g;
-    const u32x4* ksrc = reinterpret_cast<const u32x4*>(kp + off);
-    const u32x4* vsrc = reinterpret_cast<const u32x4*>(vp + off);
+    const uint16_t* kv = (role == 0 ? p.k : p.v) + b * p.k_bstride + (long)h * D_;
+    const u32x4* src = reinterpret_cast<const u32x4*>(kv + (long)(key_ok ? krow : 0) * p.rs + 8 * g);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = as_bf16x8(key_ok ? ksrc[2 * ks] : u32x4{0u, 0u, 0u, 0u});
-      vf[ks] = as_bf16x8(key_ok ? vsrc[2 * ks] : u32x4{0u, 0u, 0u, 0u});
-    }
+    for (int ks = 0; ks < NKS; ++ks) kvf[ks] = as_bf16x8(key_ok ? src[2 * ks] : u32x4{0u, 0u, 0u, 0u});
     // land these before the direct-to-LDS ring starts (see the forward kernel)
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(kvf[ks]));
   }
   const int kpos = seg_pos(p.ks, key_ok ? krow : (p.Sk - 1));
   QueryWindow qwin = query_window(p.qs, kpos, p.causal);
   if (!key_ok) qwin = QueryWindow{0, 0, 0, 0};
 
-  // key position ranges (workgroup and wave)
+  // key position ranges (workgroup and key group)
   const int wg_end = min(j0 + BKV, p.Sk);
   int kmin_wg, kmax_wg;
   seg_range(p.ks, j0, wg_end, kmin_wg, kmax_wg);
   const int kw1 = min(kw0 + 32, p.Sk);
-  const bool wave_live = kw0 < kw1;
+  const bool group_live = kw0 < kw1;
   int kmin_w = 0x7fffffff, kmax_w = 0;
-  if (wave_live) seg_range(p.ks, kw0, kw1, kmin_w, kmax_w);
+  if (group_live) seg_range(p.ks, kw0, kw1, kmin_w, kmax_w);
 
   // query tiles that may see this key block: per query segment, a suffix
   int a0 = 0, a1 = p.Sq, c0 = p.Sq, c1 = p.Sq;
@@ -202,49 +206,55 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   const int nt = nA + nC;
   auto tile_of = [&](int t) { return t < nA ? tA0 + t : tC0 + (t - nA); };
 
-  f32x16 dka[NDB], dva[NDB];
+  f32x16 acc[NDB];  // dV^T (role A) or dK^T (role B): rows = dims, columns = keys
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dka[db] = f32x16{};
-    dva[db] = f32x16{};
-  }
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  // ---- direct global -> LDS loads (lane i fills 16-byte slot i % CPR of row
-  // i / CPR, i.e. chunk slot ^ swz(row) of that row); wave 0 also moves the 32
-  // LSE and 32 Delta values of the tile (4 bytes per lane).
+  // ---- direct global -> LDS loads: load k of a tile (k = w + NW*i) moves rows
+  // [RPI*(k % (NI/2)), +RPI) of Q (k < NI/2) or dO; lane i fills 16-byte slot
+  // i % CPR of row i / CPR, i.e. chunk slot ^ swz(row).  Wave 0 also moves the
+  // 32 LSE and 32 Delta values of the tile (4 bytes per lane).
   const int dma_row = lane / CPR, dma_slot = lane % CPR;
-  uint32_t dma_off[Cfg::NQL];  // byte offset of this lane's 16 bytes within a tile whose first row is 0
+  uint32_t dma_off[Cfg::NIW];
 #pragma unroll
-  for (int it = 0; it < Cfg::NQL; ++it) {
-    const int row = RPI * (w + 4 * it) + dma_row;
-    dma_off[it] = (uint32_t)(((long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
+  for (int i = 0; i < Cfg::NIW; ++i) {
+    const int k = w + Cfg::NW * i, part = k % (Cfg::NI / 2);
+    const int row = RPI * part + dma_row;
+    dma_off[i] = (uint32_t)(((long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
   }
-  const float* stat_src = g == 0 ? lsep : delp;  // per lane: LSE (lanes 0..31) or Delta (32..63)
-  auto issue_tile = [&](auto STAGE, int t) {
-    constexpr int stage = decltype(STAGE)::value;
+  const float* stat_src = g == 0 ? lsep : delp;  // lanes 0..31: LSE, 32..63: Delta
+  auto issue_tile = [&](int stage, int t) {
     const int tt = t < nt ? t : nt - 1;  // past the end: reload the last tile into a stage nobody reads
     const int i0 = __builtin_amdgcn_readfirstlane(tile_of(tt) * BQ);
     const bool whole = i0 + BQ <= p.Sq;
-    const uint16_t* qt = qp + (long)i0 * p.rs;
-    const uint16_t* ot = op + (long)i0 * p.rs;
 #pragma unroll
-    for (int it = 0; it < Cfg::NQL; ++it) {
-      const int row0 = RPI * (w + 4 * it);
-      uint32_t off = dma_off[it];
+    for (int i = 0; i < Cfg::NIW; ++i) {
+      const int k = w + Cfg::NW * i, tns = k / (Cfg::NI / 2), part = k % (Cfg::NI / 2);
+      const int row0 = RPI * part;
+      uint32_t off = dma_off[i];
       if (!whole) {  // rows past the end load the last row; the element mask removes them
         const int row = row0 + dma_row;
-        const int i = min(row, p.Sq - 1 - i0);
-        off = (uint32_t)(((long)i * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
+        const int ii = min(row, p.Sq - 1 - i0);
+        off = (uint32_t)(((long)ii * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
       }
-      dma16_s(qt, off, &QO[stage][row0 * D]);
-      dma16_s(ot, off, &QO[stage][OT + row0 * D]);
+      dma16_s((tns ? op : qp) + (long)i0 * p.rs, off, &QO[stage][tns * OT + row0 * D]);
     }
     if (w == 0) dma4(stat_src + (long)min(i0 + ln, p.Sq - 1) * p.H, &Ss[stage][0]);
   };
-  constexpr int LOADS = 2 * Cfg::NQL;  // per tile, waves 1..3 (wave 0: one more)
+  constexpr int LOADS = Cfg::NIW;  // per tile for waves 1..7 (wave 0: one more)
+
+  auto wait_ring = [&](auto N) {  // this wave's loads of the tiles up to the one needed have landed; barrier
+    constexpr int n = decltype(N)::value;
+    if (w == 0)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n * (LOADS + 1)) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n * LOADS) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
   // per-lane LDS offsets (elements)
-  // Q / dO operand of the scores: row ln, chunk 2*ks+g = slot 2*(ks ^ qx) + (g ^ (swz & 1))
+  // operand of the score products: row ln, chunk 2*ks+g = slot 2*(ks ^ qx) + (g ^ (swz & 1))
   const int qx = swz<D>(ln) >> 1, qbase = ln * D + ((g ^ (swz<D>(ln) & 1)) << 3);
   int tofs[2][NDB];  // dO^T / Q^T transpose read: rows 8*half + trow (+16 per k-step), 32 dims per block
   {
@@ -259,58 +269,58 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       }
   }
 
-  // wave-level class of tile t: FULL (no mask) or PARTIAL (element mask).  A
-  // tile without any allowed pair for this wave is computed fully masked, which
-  // keeps the loop one straight pipeline.
+  // class of tile t for this key group: FULL (no mask) or PARTIAL (element mask).
   auto classify = [&](int t) {
     const int i0 = tile_of(t) * BQ;
-    if (!wave_live || i0 + BQ > p.Sq || kw0 + 32 > p.Sk) return (int)kPartial;
+    if (!group_live || i0 + BQ > p.Sq || kw0 + 32 > p.Sk) return (int)kPartial;
     if (!p.causal) return (int)kFull;
     int qmn, qmx;
     seg_range(p.qs, i0, i0 + BQ, qmn, qmx);
     return kmax_w <= qmn ? (int)kFull : (int)kPartial;
   };
 
-  // one k-step of S = Q K^T and dP = dO V^T for the tile in stage STAGE; output
-  // register r of lane l holds query 8*(r/4) + 4*g + r%4 of key ln
-  auto score_k = [&](auto STAGE, int ks, f32x16& s, f32x16& dp) {
-    constexpr int stage = decltype(STAGE)::value;
-    const int o = qbase + ((ks ^ qx) << 4);
-    const u32x4 aq = *reinterpret_cast<const u32x4*>(&QO[stage][o]);
-    const u32x4 ao = *reinterpret_cast<const u32x4*>(&QO[stage][OT + o]);
-    s = mfma32(as_bf16x8(aq), kf[ks], ks == 0 ? f32x16{} : s);
-    dp = mfma32(as_bf16x8(ao), vf[ks], ks == 0 ? f32x16{} : dp);
+  // one k-step of the score product with this wave's operand (S for A with Q,
+  // dP for B with dO) for the tile in stage STAGE; output register r of lane l
+  // holds query 8*(r/4) + 4*g + r%4 of key ln
+  auto score_k = [&](auto ROLE, int stage, int ks, f32x16& s) {
+    const int o = qbase + ((ks ^ qx) << 4) + decltype(ROLE)::value * OT;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(&QO[stage][o]);
+    s = mfma32(as_bf16x8(a), kvf[ks], ks == 0 ? f32x16{} : s);
   };
-  auto scores = [&](auto STAGE, f32x16& s, f32x16& dp) {
+  auto scores = [&](auto ROLE, int stage, f32x16& s) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) score_k(STAGE, ks, s, dp);
+    for (int ks = 0; ks < NKS; ++ks) score_k(ROLE, stage, ks, s);
   };
 
-  auto wait_ring = [&](auto N) {  // this wave's loads of tile t+1 have landed, then barrier
-    constexpr int n = decltype(N)::value;
-    if (w == 0)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n * (LOADS + 1)) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n * LOADS) : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+  // acc += (tile^T operand) x (bf16 packs of 16 values per lane), two 16-query k-steps;
+  // the transposed operand is dO (A: dV) or Q (B: dK) of the tile in stage STAGE
+  auto accumulate = [&](auto ROLE, int stage, const float* v) {
+    constexpr int base = decltype(ROLE)::value == 0 ? OT : 0;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int o = 8 * kk;
+      const bf16x8 pk = pack_bf16x8(v[o], v[o + 1], v[o + 2], v[o + 3], v[o + 4], v[o + 5], v[o + 6], v[o + 7]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2 lo = ds_read_tr16(&QO[stage][base + tofs[0][db] + 16 * kk * D]);
+        const u32x2 hi = ds_read_tr16(&QO[stage][base + tofs[1][db] + 16 * kk * D]);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        acc[db] = mfma32(as_bf16x8(a), pk, acc[db]);
+      }
+    }
   };
 
   const float c = p.c;
   constexpr float NEG_INF = -__builtin_inff();
+  using RA = std::integral_constant<int, 0>;
+  using RB = std::integral_constant<int, 1>;
 
-  // one pipeline step: P, dS and the dV/dK products of tile t (scores in
-  // s_cur/dp_cur, stage STAGE) interleaved with the score products of tile t+1
-  auto step = [&](auto STAGE, int t, f32x16& s_cur, f32x16& dp_cur, int& cls_cur, f32x16& s_nx, f32x16& dp_nx,
-                  int& cls_nx) {
-    constexpr int stage = decltype(STAGE)::value;
-    constexpr int nstage = (stage + 1) % NST, fstage = (stage + NST - 1) % NST;
-    wait_ring(std::integral_constant<int, NST - 3>{});
-    issue_tile(std::integral_constant<int, fstage>{}, t + NST - 1);
+  // ---- role A, step t: P(t) from the scores of tile t (in s_cur), interleaved
+  // with the scores of tile t+1; publish P(t); dV^T += dO(t)^T P(t)
+  auto step_a = [&](int stage, int t, f32x16& s_cur, int& cls_cur, f32x16& s_nx, int& cls_nx) {
+    const int nstage = stage + 1 == NST ? 0 : stage + 1;
     const int i0 = tile_of(t) * BQ;
     cls_nx = t + 1 < nt ? classify(t + 1) : (int)kFull;
-
-    // element mask of a partial tile: masked scores become -inf (probability 0)
     if (cls_cur == kPartial) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -318,84 +328,112 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         s_cur[r] = in_window(qwin, i) ? s_cur[r] : NEG_INF;
       }
     }
-
-    // One straight-line block: the score products of tile t+1 (matrix cores)
-    // interleave with P and dS of tile t (vector ALUs).  The LSE enters as
-    // -LSE*log2(e), clamped so that a row without any allowed key (LSE = -inf)
-    // still gives exp2(-inf) = 0 on its (masked) scores.
-    float pv[16], dsv[16];
+    // the LSE of the tile's rows is already in base-2 units (see to_log2 below)
+    float pv[16];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      score_k(std::integral_constant<int, nstage>{}, ks, s_nx, dp_nx);
+      score_k(RA{}, nstage, ks, s_nx);
 #pragma unroll
       for (int u = 0; u < 16 / NKS; ++u) {
         const int r = (16 / NKS) * ks + u;
-        const int qi = 8 * (r >> 2) + 4 * g + (r & 3);
-        const float nl = fminf(Ss[stage][qi] * -kLog2e, 3.0e38f);
-        const float x = fast_exp2(__builtin_fmaf(s_cur[r], c, nl));
-        pv[r] = x;
-        dsv[r] = x * (dp_cur[r] - Ss[stage][BQ + qi]);
+        pv[r] = fast_exp2(__builtin_fmaf(s_cur[r], c, -Ss[stage][8 * (r >> 2) + 4 * g + (r & 3)]));
       }
     }
-    // dV^T += dO^T P ; dK^T += Q^T dS over two 16-query k-steps
+    float* pdst = &Ps[t & 1][kw][0][lane][0];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int o = 8 * kk;
-      const bf16x8 pb = pack_bf16x8(pv[o], pv[o + 1], pv[o + 2], pv[o + 3], pv[o + 4], pv[o + 5], pv[o + 6], pv[o + 7]);
-      const bf16x8 sb =
-          pack_bf16x8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5], dsv[o + 6], dsv[o + 7]);
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<f32x4*>(pdst + m * 256) = f32x4{pv[4 * m], pv[4 * m + 1], pv[4 * m + 2], pv[4 * m + 3]};
+    accumulate(RA{}, stage, pv);
+  };
+
+  // ---- role B, step t: dP(t) (into dp_nx) interleaved with dS(t-1) from P(t-1)
+  // and dP(t-1) (in dp_cur); dK^T += Q(t-1)^T dS(t-1).  PSTAGE = stage of t-1.
+  auto step_b = [&](int stage, int pstage, auto DO_DP, int t, f32x16& dp_cur, f32x16& dp_nx) {
+    constexpr bool do_dp = decltype(DO_DP)::value;  // false: last step, no tile t
+    const bool prev = t > 0;
+    float dsv[16];
+    const float* psrc = &Ps[(t + 1) & 1][kw][0][lane][0];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2 olo = ds_read_tr16(&QO[stage][OT + tofs[0][db] + 16 * kk * D]);
-        const u32x2 ohi = ds_read_tr16(&QO[stage][OT + tofs[1][db] + 16 * kk * D]);
-        const u32x4 ao = {olo[0], olo[1], ohi[0], ohi[1]};
-        dva[db] = mfma32(as_bf16x8(ao), pb, dva[db]);
-        const u32x2 qlo = ds_read_tr16(&QO[stage][tofs[0][db] + 16 * kk * D]);
-        const u32x2 qhi = ds_read_tr16(&QO[stage][tofs[1][db] + 16 * kk * D]);
-        const u32x4 aq = {qlo[0], qlo[1], qhi[0], qhi[1]};
-        dka[db] = mfma32(as_bf16x8(aq), sb, dka[db]);
+    for (int ks = 0; ks < NKS; ++ks) {
+      if constexpr (do_dp) score_k(RB{}, stage, ks, dp_nx);
+#pragma unroll
+      for (int u = 0; u < 16 / NKS; ++u) {
+        const int r = (16 / NKS) * ks + u;
+        const float pr = psrc[(r >> 2) * 256 + (r & 3)];
+        dsv[r] = pr * (dp_cur[r] - Ss[pstage][BQ + 8 * (r >> 2) + 4 * g + (r & 3)]);
       }
+    }
+    if (prev) accumulate(RB{}, pstage, dsv);
+  };
+
+  // Wave 0, which loads the per-row statistics, rewrites the LSE of a resident
+  // tile in base-2 units (-inf, a row without any allowed key, becomes +inf so
+  // that its recomputed probabilities are exactly 0); the next barrier
+  // publishes the converted values.
+  auto to_log2 = [&](int stage) {
+    if (w == 0 && g == 0) {
+      const float l = Ss[stage][ln];
+      Ss[stage][ln] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
     }
   };
 
   if (nt > 0) {
-    static_assert(NST == 4, "the loop below is unrolled for a ring of 4 stages");
-    issue_tile(std::integral_constant<int, 0>{}, 0);
-    issue_tile(std::integral_constant<int, 1>{}, 1);
-    issue_tile(std::integral_constant<int, 2>{}, 2);
-    wait_ring(std::integral_constant<int, NST - 2>{});
-    int cls_a = classify(0), cls_b = kFull;
-    f32x16 s_a, dp_a, s_b, dp_b;
-    scores(std::integral_constant<int, 0>{}, s_a, dp_a);
-    for (int t = 0; t < nt; t += 4) {
-      step(std::integral_constant<int, 0>{}, t, s_a, dp_a, cls_a, s_b, dp_b, cls_b);
+    constexpr int AHEAD = NST - 4;  // tiles still in flight when tile t+1 must be resident
+    for (int i = 0; i < NST - 2; ++i) issue_tile(i, i);
+    wait_ring(std::integral_constant<int, AHEAD>{});  // tiles 0 and 1 resident
+    to_log2(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // Step t reads tiles t-1, t, t+1 and loads tile t+NST-2 into the stage of
+    // tile t-2.  Unrolled by two so that the two score buffers alternate.
+    f32x16 sa, sb;  // role A: scores; role B: dP
+    int ca = kFull, cb = kFull;
+    if (role == 0) {
+      ca = classify(0);
+      scores(RA{}, 0, sa);
+    }
+    int st = 0;  // stage of tile t
+    auto body = [&](int t, f32x16& x_cur, int& c_cur, f32x16& x_nx, int& c_nx) {
+      if (t > 0) wait_ring(std::integral_constant<int, AHEAD>{});  // tile t+1 resident; all past step t-1
+      const int sp = st == 0 ? NST - 1 : st - 1;
+      const int sf = st >= 2 ? st - 2 : st + NST - 2;
+      issue_tile(sf, t + NST - 2);
+      to_log2(st + 1 == NST ? 0 : st + 1);  // tile t+1, read from step t+1 on
+      if (role == 0)
+        step_a(st, t, x_cur, c_cur, x_nx, c_nx);
+      else
+        step_b(st, sp, std::true_type{}, t, x_cur, x_nx);
+      st = st + 1 == NST ? 0 : st + 1;
+    };
+    for (int t = 0; t < nt; t += 2) {
+      body(t, sa, ca, sb, cb);
       if (t + 1 >= nt) break;
-      step(std::integral_constant<int, 1>{}, t + 1, s_b, dp_b, cls_b, s_a, dp_a, cls_a);
-      if (t + 2 >= nt) break;
-      step(std::integral_constant<int, 2>{}, t + 2, s_a, dp_a, cls_a, s_b, dp_b, cls_b);
-      if (t + 3 >= nt) break;
-      step(std::integral_constant<int, 3>{}, t + 3, s_b, dp_b, cls_b, s_a, dp_a, cls_a);
+      body(t + 1, sb, cb, sa, ca);
+    }
+    // role B's last step: dS and dK of tile nt-1 (P(nt-1) published in step nt-1)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (role == 1) {
+      f32x16 last = (nt % 2 == 1) ? sb : sa;  // dP(nt-1): into sb for even nt-1, sa for odd
+      f32x16 dummy;
+      const int sp = st == 0 ? NST - 1 : st - 1;  // st is now the stage of tile nt
+      step_b(st, sp, std::false_type{}, nt, last, dummy);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // retire the trailing (unused) loads
   }
 
   if (!key_ok || nt == 0) return;
-  float* dkp = p.dk + b * p.k_bstride + (long)h * D_ + (long)krow * p.rs;
-  float* dvp = p.dv + b * p.k_bstride + (long)h * D_ + (long)krow * p.rs;
+  float* dst = (role == 0 ? p.dv : p.dk) + b * p.k_bstride + (long)h * D_ + (long)krow * p.rs;
+  const float mul = role == 0 ? 1.f : p.scale;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d0 = 32 * db + 8 * q4 + 4 * g;
-      f32x4 k4 = *reinterpret_cast<f32x4*>(dkp + d0);
-      f32x4 v4 = *reinterpret_cast<f32x4*>(dvp + d0);
+      f32x4 v4 = *reinterpret_cast<f32x4*>(dst + d0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        k4[e] += p.scale * dka[db][4 * q4 + e];
-        v4[e] += dva[db][4 * q4 + e];
-      }
-      *reinterpret_cast<f32x4*>(dkp + d0) = k4;
-      *reinterpret_cast<f32x4*>(dvp + d0) = v4;
+      for (int e = 0; e < 4; ++e) v4[e] += mul * acc[db][4 * q4 + e];
+      *reinterpret_cast<f32x4*>(dst + d0) = v4;
     }
 }
 
