@@ -45,24 +45,28 @@ struct FwdParams {
 #ifndef EA_FWD_LDS_AHEAD
 #define EA_FWD_LDS_AHEAD 0  // >0: schedule hints with this many LDS reads ahead (0: compiler default)
 #endif
+#ifndef EA_FWD_NW
+#define EA_FWD_NW 4  // waves per workgroup (32 query rows each)
+#endif
 #ifndef EA_FWD_NST
 #define EA_FWD_NST 4  // LDS stages of the key/value ring (tiles in flight: NST - 1)
 #endif
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BQ = 128, BK = 32, NT = 256, NST = EA_FWD_NST;
+  static constexpr int NW = EA_FWD_NW, BQ = 32 * NW, BK = 32, NT = 64 * NW, NST = EA_FWD_NST;
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;       // rows one wave covers per direct-to-LDS load
-  static constexpr int NKL = BK / (4 * RPI); // direct-to-LDS loads per thread per tile (each of K and V)
+  static constexpr int NLT = BK / RPI;                // direct-to-LDS loads per tile (each of K and V)
+  static constexpr int NKL = (NLT + NW - 1) / NW;     // per wave (waves w + NW*i < NLT take part)
   static constexpr int LDS_T = BK * D;
-  static_assert(NKL >= 1 && NKL * 4 * RPI == BK, "unsupported key tile");
+  static_assert(NLT * RPI == BK && (NLT % NW == 0 || NLT < NW), "unsupported key tile");
 };
 
 // Rows of a key/value tile that lie past the end of the keys load the last key
 // row instead (so every address is valid); the score mask removes them.
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * EA_FWD_NW, 8 / EA_FWD_NW) void fwd_kernel(FwdParams p) {
   using Cfg = FwdCfg<D>;
   constexpr int BQ = Cfg::BQ, BK = Cfg::BK, CPR = Cfg::CPR, NST = Cfg::NST, RPI = Cfg::RPI;
   constexpr int NKS = D / 16, NDB = D / 32;
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   long dma_off[Cfg::NKL];  // element offset of this lane's 16 bytes within a tile whose first row is 0
 #pragma unroll
   for (int it = 0; it < Cfg::NKL; ++it) {
-    const int row = RPI * (w + 4 * it) + dma_row;
+    const int row = RPI * (w + Cfg::NW * it) + dma_row;
     dma_off[it] = (long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3);
   }
   auto issue_tile = [&](auto STAGE, int t) {
@@ -153,7 +157,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     const bool whole = j0 + BK <= p.Sk;
 #pragma unroll
     for (int it = 0; it < Cfg::NKL; ++it) {
-      const int row0 = RPI * (w + 4 * it);
+      if (Cfg::NLT < Cfg::NW && w >= Cfg::NLT) break;  // this wave loads nothing (waits on vmcnt pass at once)
+      const int row0 = RPI * (w + Cfg::NW * it);
       long off = (long)j0 * p.rs + dma_off[it];
       if (!whole) {
         const int row = row0 + dma_row;
@@ -370,7 +375,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.nqb = (a.Sq + BQ - 1) / BQ;
   const long nwg = (long)a.B * a.H * p.nqb;
   if (nwg == 0) return hipSuccess;
-  dim3 grid((unsigned)nwg), block(256);
+  dim3 grid((unsigned)nwg), block(FwdCfg<128>::NT);
   if (a.D == 64)
     hipLaunchKernelGGL(fwd_kernel<64>, grid, block, 0, stream, p);
   else
