@@ -18,6 +18,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results stay in vector registers (the softmax rescale and the
+    # probability math work on them) instead of round trips through the
+    # accumulation registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-variable", "-Wno-unused-function",
 ]
 

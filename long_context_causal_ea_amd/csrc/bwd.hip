@@ -27,12 +27,6 @@
 #include "ea_launch.h"
 
 // Tile and occupancy choices (workgroups per CU the register budget is sized for).
-#ifndef EA_DQ_BK
-#define EA_DQ_BK 32
-#endif
-#ifndef EA_DQ_MIN_WG
-#define EA_DQ_MIN_WG 2
-#endif
 
 namespace ea {
 
@@ -438,23 +432,33 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------ dQ
+// One workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
+// 32 rows and keeps their Q and dO rows as MFMA B operands and its dQ^T
+// accumulator in registers.  Key/value tiles of 32 rows stream through a
+// 4-stage direct-to-LDS ring (K and V of a stage side by side), three tiles in
+// flight, exactly like the forward.  Per tile: S^T = K Q^T and dP^T = V dO^T
+// (query on the lane axis, so each lane's LSE and Delta are one value), P and
+// dS = P (dP - Delta), then dQ^T += K^T dS^T with K^T read by the LDS transpose
+// read.  The score products of tile t+1 interleave with the P / dS arithmetic
+// of tile t.
 template <int D>
 struct DqCfg {
-  static constexpr int BQ = 128, BK = EA_DQ_BK, NT = 256;
-  static constexpr int NMB = BK / 32, NKB = BK / 16;
-  static constexpr int CPR = D / 8;
-  static constexpr int NKL = BK * CPR / NT;  // 16-byte chunks per thread per tile (each of K and V)
+  static constexpr int NW = 4, BQ = 32 * NW, BK = 32, NT = 64 * NW, NST = 4;
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;             // rows one direct-to-LDS load covers
+  static constexpr int NLT = BK / RPI;             // loads per tile (each of K and V)
+  static constexpr int NKL = (NLT + NW - 1) / NW;  // per wave (waves w + NW*i < NLT take part)
   static constexpr int LDS_T = BK * D;
-  static_assert(BK % 32 == 0 && NKL * NT == BK * CPR, "unsupported key tile");
+  static_assert(NLT * RPI == BK && (NLT % NW == 0 || NLT < NW), "unsupported key tile");
 };
 
 template <int D>
-__global__ __launch_bounds__(256, EA_DQ_MIN_WG) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   using Cfg = DqCfg<D>;
-  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, CPR = Cfg::CPR;
-  constexpr int NKS = D / 16, NDB = D / 32, NMB = Cfg::NMB, NKB = Cfg::NKB;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][Cfg::LDS_T];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][Cfg::LDS_T];
+  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, CPR = Cfg::CPR, NST = Cfg::NST, RPI = Cfg::RPI;
+  constexpr int NKS = D / 16, NDB = D / 32, KT = Cfg::LDS_T;
+  // stage s: K tile at KV[s][0], V tile at KV[s][KT]
+  __shared__ __attribute__((aligned(16))) uint16_t KV[NST][2 * KT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
@@ -462,7 +466,7 @@ __global__ __launch_bounds__(256, EA_DQ_MIN_WG) void dq_kernel(BwdParams p) {
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = work / p.nblk;
-  const int qb = p.nblk - 1 - work % p.nblk;
+  const int qb = p.nblk - 1 - work % p.nblk;  // longest query blocks first
   const int b = bh / p.H, h = bh % p.H;
   const int D_ = D;
 
@@ -475,6 +479,7 @@ __global__ __launch_bounds__(256, EA_DQ_MIN_WG) void dq_kernel(BwdParams p) {
   const int qrow = i0 + 32 * w + ln;
   const bool row_ok = qrow < p.Sq;
 
+  // this lane's Q and dO rows as MFMA B operands: dims 16*ks + 8*g .. +7
   bf16x8 qf[NKS], of[NKS];
   {
     const long off = (long)(row_ok ? qrow : 0) * p.rs + 8 * g;
@@ -489,6 +494,11 @@ __global__ __launch_bounds__(256, EA_DQ_MIN_WG) void dq_kernel(BwdParams p) {
   const long srow = b * p.row_bstride + (long)(row_ok ? qrow : 0) * p.H + h;
   const float lse2 = row_ok ? lse_to_log2(p.lse[srow]) : __builtin_inff();
   const float dlt = row_ok ? p.delta[srow] : 0.f;
+  // land these before the direct-to-LDS ring starts (see the forward kernel)
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qf[ks]), "+v"(of[ks]));
+  float l2 = lse2, dl = dlt;
+  asm volatile("" : "+v"(l2), "+v"(dl));
   const int qpos = seg_pos(p.qs, row_ok ? qrow : (p.Sq - 1));
   const KeyWindow kwin = key_window(p.ks, qpos, p.causal);
 
@@ -514,104 +524,141 @@ __global__ __launch_bounds__(256, EA_DQ_MIN_WG) void dq_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqa[db] = f32x16{};
 
-  // staging: consecutive threads take consecutive 16-byte chunks of a row
-  u32x4 kreg[Cfg::NKL], vreg[Cfg::NKL];
-
-  auto load_tile = [&](int jt) {
-    const int j0 = jt * BK;
+  // ---- direct global -> LDS loads (as in the forward); rows past the end of
+  // the keys load the last key row, and the element mask removes them
+  const int dma_row = lane / CPR, dma_slot = lane % CPR;
+  long dma_off[Cfg::NKL];
+#pragma unroll
+  for (int it = 0; it < Cfg::NKL; ++it) {
+    const int row = RPI * (w + Cfg::NW * it) + dma_row;
+    dma_off[it] = (long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3);
+  }
+  auto issue_tile = [&](auto STAGE, int t) {
+    constexpr int stage = decltype(STAGE)::value;
+    const int tt = t < nt ? t : nt - 1;  // past the end: reload the last tile into a stage nobody reads
+    const int j0 = tile_of(tt) * BK;
+    const bool whole = j0 + BK <= p.Sk;
 #pragma unroll
     for (int it = 0; it < Cfg::NKL; ++it) {
-      const int c = tid + Cfg::NT * it;
-      const int row = c / CPR, col = c % CPR;
-      const int j = j0 + row;
-      const long off = (long)j * p.rs + col * 8;
-      kreg[it] = j < p.Sk ? *reinterpret_cast<const u32x4*>(kp + off) : u32x4{0u, 0u, 0u, 0u};
-      vreg[it] = j < p.Sk ? *reinterpret_cast<const u32x4*>(vp + off) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < Cfg::NKL; ++it) {
-      const int c = tid + Cfg::NT * it;
-      const int o = tile_off<D>(c / CPR, c % CPR);
-      *reinterpret_cast<u32x4*>(&Ks[buf][o]) = kreg[it];
-      *reinterpret_cast<u32x4*>(&Vs[buf][o]) = vreg[it];
-    }
-  };
-
-  const int swk = swz<D>(ln);                                  // K/V operand rows are mb*32 + ln
-  const int trow = 4 * g + ((lane & 15) >> 2);                 // transpose read: row within a 16-key step
-  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // transpose read: column within 32 dims
-
-  if (nt > 0) load_tile(tile_of(0));
-
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    const int jt = tile_of(t);
-    const int j0 = jt * BK;
-    store_tile(buf);
-    __syncthreads();
-    if (t + 1 < nt) load_tile(tile_of(t + 1));
-
-    int cls = kSkip;
-    if (wave_live) {
-      const int jend = min(j0 + BK, p.Sk);
-      int kmn, kmx;
-      seg_range(p.ks, j0, jend, kmn, kmx);
-      const bool tail = j0 + BK > p.Sk;
-      if (!p.causal) cls = tail ? kPartial : kFull;
-      else if (kmn > qmax_w) cls = kSkip;
-      else if (kmx <= qmin_w && !tail) cls = kFull;
-      else cls = kPartial;
-    }
-    if (cls == kSkip) continue;
-
-    f32x16 st[NMB], dpt[NMB];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      st[mb] = f32x16{};
-      dpt[mb] = f32x16{};
-      const uint16_t* krow = &Ks[buf][(mb * 32 + ln) * D];
-      const uint16_t* vrow = &Vs[buf][(mb * 32 + ln) * D];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int o = ((2 * ks + g) ^ swk) << 3;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + o);
-        st[mb] = mfma32(as_bf16x8(a), qf[ks], st[mb]);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(vrow + o);
-        dpt[mb] = mfma32(as_bf16x8(b), of[ks], dpt[mb]);
+      if (Cfg::NLT < Cfg::NW && w >= Cfg::NLT) break;  // this wave loads nothing
+      const int row0 = RPI * (w + Cfg::NW * it);
+      long off = (long)j0 * p.rs + dma_off[it];
+      if (!whole) {
+        const int row = row0 + dma_row;
+        const int j = min(j0 + row, p.Sk - 1);
+        off = (long)j * p.rs + ((dma_slot ^ swz<D>(row)) << 3);
       }
+      dma16(kp + off, &KV[stage][row0 * D]);
+      dma16(vp + off, &KV[stage][KT + row0 * D]);
     }
+  };
+  constexpr int LOADS_PER_TILE = 2 * Cfg::NKL;
 
-    bf16x8 sb[NKB];
+  // per-lane LDS offsets: K / V operand row ln, chunk 2*ks+g = slot 2*(ks ^ kx) + (g ^ (swz & 1))
+  const int kx = swz<D>(ln) >> 1, kbase = ln * D + ((g ^ (swz<D>(ln) & 1)) << 3);
+  int tofs[2][NDB];  // K^T transpose read: rows 8*half + trow (+16 per k-step), 32 dims per block
+  {
+    const int trow = 4 * g + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = 32 * db + tcol;
+        tofs[half][db] = tile_off<D>(8 * half + trow, col >> 3) + (col & 7);
+      }
+  }
+
+  // wave-level class of tile t: FULL or PARTIAL (a tile without any allowed pair
+  // is computed fully masked, keeping the loop one straight pipeline)
+  auto classify = [&](int t) {
+    const int j0 = tile_of(t) * BK;
+    if (!wave_live || j0 + BK > p.Sk) return (int)kPartial;
+    if (!p.causal) return (int)kFull;
+    int kmn, kmx;
+    seg_range(p.ks, j0, j0 + BK, kmn, kmx);
+    return kmx <= qmin_w ? (int)kFull : (int)kPartial;
+  };
+
+  // S^T = K Q^T and dP^T = V dO^T of the tile in stage STAGE; register r of lane
+  // l holds key 8*(r/4) + 4*g + r%4 of query ln
+  auto score_k = [&](auto STAGE, int ks, f32x16& s, f32x16& dp) {
+    constexpr int stage = decltype(STAGE)::value;
+    const int o = kbase + ((ks ^ kx) << 4);
+    const u32x4 a = *reinterpret_cast<const u32x4*>(&KV[stage][o]);
+    s = mfma32(as_bf16x8(a), qf[ks], ks == 0 ? f32x16{} : s);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&KV[stage][KT + o]);
+    dp = mfma32(as_bf16x8(v), of[ks], ks == 0 ? f32x16{} : dp);
+  };
+
+  constexpr float NEG_INF = -__builtin_inff();
+  const float c = p.c;
+
+  auto step = [&](auto STAGE, int t, f32x16& s_cur, f32x16& dp_cur, int& cls_cur, f32x16& s_nx, f32x16& dp_nx,
+                  int& cls_nx) {
+    constexpr int stage = decltype(STAGE)::value;
+    constexpr int nstage = (stage + 1) % NST, fstage = (stage + NST - 1) % NST;
+    lds_ring_sync<(NST - 3) * LOADS_PER_TILE>();  // tile t+1 resident; all done with stage (t-1) % NST
+    issue_tile(std::integral_constant<int, fstage>{}, t + NST - 1);
+    const int j0 = tile_of(t) * BK;
+    cls_nx = t + 1 < nt ? classify(t + 1) : (int)kFull;
+    if (cls_cur == kPartial) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(__builtin_fmaf(st[mb][r], p.c, -lse2));
-        if (cls == kPartial) pv = in_window(kwin, j0 + mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) ? pv : 0.f;
-        st[mb][r] = pv * (dpt[mb][r] - dlt);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int o = 8 * kk;
-        sb[2 * mb + kk] = pack_bf16x8(st[mb][o], st[mb][o + 1], st[mb][o + 2], st[mb][o + 3], st[mb][o + 4],
-                                      st[mb][o + 5], st[mb][o + 6], st[mb][o + 7]);
+        const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        s_cur[r] = in_window(kwin, j) ? s_cur[r] : NEG_INF;
       }
     }
-
+    // scores of tile t+1 interleaved with dS of tile t (lse2 = +inf for a row
+    // without any allowed key, so its probabilities are exactly 0)
+    float dsv[16];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      score_k(std::integral_constant<int, nstage>{}, ks, s_nx, dp_nx);
+#pragma unroll
+      for (int u = 0; u < 16 / NKS; ++u) {
+        const int r = (16 / NKS) * ks + u;
+        const float pr = fast_exp2(__builtin_fmaf(s_cur[r], c, -l2));
+        dsv[r] = pr * (dp_cur[r] - dl);
+      }
+    }
+    const bf16x8 sb0 = pack_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+    const bf16x8 sb1 = pack_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
     // dQ^T += K^T dS^T; K^T read transposed from the row-major K tile
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int col = db * 32 + tcol;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x2 lo = ds_read_tr16(&Ks[buf][tile_off<D>(kb * 16 + trow, col >> 3) + (col & 7)]);
-        const u32x2 hi = ds_read_tr16(&Ks[buf][tile_off<D>(kb * 16 + 8 + trow, col >> 3) + (col & 7)]);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        dqa[db] = mfma32(as_bf16x8(a), sb[kb], dqa[db]);
-      }
+      const u32x2 lo0 = ds_read_tr16(&KV[stage][tofs[0][db]]);
+      const u32x2 hi0 = ds_read_tr16(&KV[stage][tofs[1][db]]);
+      const u32x2 lo1 = ds_read_tr16(&KV[stage][tofs[0][db] + 16 * D]);
+      const u32x2 hi1 = ds_read_tr16(&KV[stage][tofs[1][db] + 16 * D]);
+      const u32x4 a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
+      const u32x4 a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
+      dqa[db] = mfma32(as_bf16x8(a0), sb0, dqa[db]);
+      dqa[db] = mfma32(as_bf16x8(a1), sb1, dqa[db]);
     }
+  };
+
+  if (nt > 0) {
+    static_assert(NST == 4, "the loop below is unrolled for a ring of 4 stages");
+    using S0 = std::integral_constant<int, 0>;
+    issue_tile(S0{}, 0);
+    issue_tile(std::integral_constant<int, 1>{}, 1);
+    issue_tile(std::integral_constant<int, 2>{}, 2);
+    lds_ring_sync<(NST - 2) * LOADS_PER_TILE>();
+    int cls_a = classify(0), cls_b = kFull;
+    f32x16 s_a, dp_a, s_b, dp_b;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) score_k(S0{}, ks, s_a, dp_a);
+    for (int t = 0; t < nt; t += 4) {
+      step(S0{}, t, s_a, dp_a, cls_a, s_b, dp_b, cls_b);
+      if (t + 1 >= nt) break;
+      step(std::integral_constant<int, 1>{}, t + 1, s_b, dp_b, cls_b, s_a, dp_a, cls_a);
+      if (t + 2 >= nt) break;
+      step(std::integral_constant<int, 2>{}, t + 2, s_a, dp_a, cls_a, s_b, dp_b, cls_b);
+      if (t + 3 >= nt) break;
+      step(std::integral_constant<int, 3>{}, t + 3, s_b, dp_b, cls_b, s_a, dp_a, cls_a);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // retire the trailing (unused) loads
   }
 
   if (!row_ok || nt == 0) return;
@@ -691,7 +738,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   BwdParams p = make_params(a);
-  p.nblk = (a.Sq + 127) / 128;
+  p.nblk = (a.Sq + DqCfg<128>::BQ - 1) / DqCfg<128>::BQ;
   const long nwg = (long)a.B * a.H * p.nblk;
   if (nwg == 0 || a.Sk == 0) return hipSuccess;
   dim3 grid((unsigned)nwg), block(256);
