@@ -4,12 +4,11 @@
 // staged on chip and the softmax is accumulated tile by tile).
 //
 // gfx950 mapping
-//  - One workgroup = 4 waves of one (batch, head); each wave owns RB blocks of
-//    32 query rows (default RB = 1: 128 rows, two workgroups per CU).  With
-//    RB = 2 every K and V operand read feeds two matrix-core products, but one
-//    wave per SIMD hides latency worse (measured slower on MI355X).
-//    Key/value tiles of 32 rows stream through a ring of LDS stages filled by
-//    direct global->LDS loads, three tiles in flight.
+//  - One workgroup = 8 waves = 256 query rows of one (batch, head), one
+//    workgroup (two waves per SIMD) per CU; each wave owns 32 rows.  Key/value
+//    tiles of 64 rows (two 32-key blocks) stream through a ring of LDS stages
+//    filled by direct global->LDS loads, three tiles in flight, so one barrier
+//    covers 32 matrix-core products per wave.
 //  - The loop is software-pipelined: the scores of tile t+1 are issued to the
 //    matrix cores while the softmax of tile t runs on the vector ALUs.
 //  - Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
@@ -46,10 +45,10 @@ struct FwdParams {
 };
 
 #ifndef EA_FWD_NW
-#define EA_FWD_NW 4  // waves per workgroup
+#define EA_FWD_NW 8  // waves per workgroup (32 query rows each)
 #endif
-#ifndef EA_FWD_RB
-#define EA_FWD_RB 1  // blocks of 32 query rows per wave (2: one workgroup per CU, measured slower)
+#ifndef EA_FWD_NMB
+#define EA_FWD_NMB 2  // 32-key blocks per key/value tile
 #endif
 #ifndef EA_FWD_NST
 #define EA_FWD_NST 4  // LDS stages of the key/value ring (tiles in flight: NST - 1)
@@ -57,15 +56,14 @@ struct FwdParams {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int NW = EA_FWD_NW, RB = EA_FWD_RB, BQ = 32 * NW * RB, BK = 32, NT = 64 * NW;
+  static constexpr int NW = EA_FWD_NW, NMB = EA_FWD_NMB, BQ = 32 * NW, BK = 32 * NMB, NT = 64 * NW;
   static constexpr int NST = EA_FWD_NST;
   static constexpr int CPR = D / 8;                   // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;                // rows one wave covers per direct-to-LDS load
   static constexpr int NLT = BK / RPI;                // direct-to-LDS loads per tile (each of K and V)
   static constexpr int NKL = (NLT + NW - 1) / NW;     // per wave (waves w + NW*i < NLT take part)
   static constexpr int LDS_T = BK * D;
-  // workgroups per CU the register budget is sized for: RB = 1 fits two
-  static constexpr int MIN_WG = RB == 1 ? 8 / NW : 1;
+  static constexpr int MIN_WG = NW >= 8 ? 1 : 2;      // workgroups per CU (two waves per SIMD)
   static_assert(NLT * RPI == BK && (NLT % NW == 0 || NLT < NW), "unsupported key tile");
 };
 
@@ -74,7 +72,7 @@ struct FwdCfg {
 template <int D>
 __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kernel(FwdParams p) {
   using Cfg = FwdCfg<D>;
-  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, CPR = Cfg::CPR, NST = Cfg::NST, RPI = Cfg::RPI, RB = Cfg::RB;
+  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, CPR = Cfg::CPR, NST = Cfg::NST, RPI = Cfg::RPI, NMB = Cfg::NMB;
   constexpr int NKS = D / 16, NDB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NST][Cfg::LDS_T];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NST][Cfg::LDS_T];
@@ -95,49 +93,34 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   const uint16_t* vp = p.v + b * p.k_bstride + (long)h * D_;
 
   const int i0 = qb * BQ;
-  const int r0w = i0 + w * 32 * RB;  // first query row of this wave; row block rb covers r0w + 32*rb ..
+  const int qrow = i0 + w * 32 + ln;
+  const bool row_ok = qrow < p.Sq;
 
-  // ---- this lane's query rows in MFMA B-operand form (8 dims per k-step), one per row block
-  bf16x8 qf[RB][NKS];
-  KeyWindow kwin[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int qrow = r0w + 32 * rb + ln;
-    const bool ok = qrow < p.Sq;
-    const u32x4* src = reinterpret_cast<const u32x4*>(qp + (long)(ok ? qrow : 0) * p.rs + 8 * g);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = as_bf16x8(ok ? src[2 * ks] : u32x4{0u, 0u, 0u, 0u});
-    kwin[rb] = key_window(p.ks, seg_pos(p.qs, ok ? qrow : (p.Sq - 1)), p.causal);
-  }
-  // land the Q rows before the direct-to-LDS ring starts: the compiler cannot
-  // see those loads and would otherwise wait for all of them at each use of Q.
-  // With several row blocks the Q operands live in the accumulation registers
-  // (the matrix cores read them from there), leaving the vector registers to
-  // the O accumulators, which the softmax rescale touches.
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  // ---- this lane's query row in MFMA B-operand form (8 dims per k-step)
+  bf16x8 qf[NKS];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(qp + (long)(row_ok ? qrow : 0) * p.rs + 8 * g);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      if constexpr (RB > 1)
-        asm volatile("" : "+a"(qf[rb][ks]));
-      else
-        asm volatile("" : "+v"(qf[rb][ks]));
+      u32x4 u = row_ok ? src[2 * ks] : u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = as_bf16x8(u);
     }
+    // land the Q rows before the direct-to-LDS ring starts: the compiler cannot
+    // see those loads and would otherwise wait for all of them at each use of Q
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qf[ks]));
+  }
+  const int qpos = seg_pos(p.qs, row_ok ? qrow : (p.Sq - 1));
+  const KeyWindow kwin = key_window(p.ks, qpos, p.causal);
 
-  // ---- position ranges of the workgroup's and each row block's valid rows
+  // ---- position ranges of the workgroup's and this wave's valid rows
   const int wg_end = min(i0 + BQ, p.Sq);
   int qmin_wg, qmax_wg;
   seg_range(p.qs, i0, wg_end, qmin_wg, qmax_wg);
-  bool blk_live[RB];
-  int qmin_b[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int a = r0w + 32 * rb, e = min(a + 32, p.Sq);
-    blk_live[rb] = a < e;
-    int mx = -1;
-    qmin_b[rb] = 0;
-    if (blk_live[rb]) seg_range(p.qs, a, e, qmin_b[rb], mx);
-  }
+  const int w0 = i0 + w * 32, w1 = min(w0 + 32, p.Sq);
+  const bool wave_live = w0 < w1;
+  int qmin_w = 0, qmax_w = -1;
+  if (wave_live) seg_range(p.qs, w0, w1, qmin_w, qmax_w);
 
   // ---- key tiles to visit: up to two contiguous runs
   int e0 = p.Sk, b1 = p.Sk, e1 = p.Sk;
@@ -156,15 +139,10 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   // than 8 (in log2 units): probabilities then stay below 2^8, exactly
   // representable in the accumulation, and the rescale of O is rare.
   const float raise_thr = 8.f / p.c;
-  float m_run[RB], l_run[RB];
-  f32x16 oacc[RB][NDB];
+  float m_run = NEG_INF, l_run = 0.f;
+  f32x16 oacc[NDB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = NEG_INF;
-    l_run[rb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[rb][db] = f32x16{};
-  }
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
 
   // ---- direct global -> LDS loads: one instruction moves 16 bytes per lane into
   // 64 consecutive 16-byte LDS slots (RPI rows); lane i fills slot i % CPR of row
@@ -198,9 +176,9 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   constexpr int LOADS_PER_TILE = 2 * Cfg::NKL;
 
   // per-lane LDS offsets (elements), fixed for the whole kernel
-  // K operand: row ln, chunk 2*ks+g, i.e. slot (2*ks+g) ^ swz(ln) = 2*(ks ^ kx) + kg
+  // K operand: row ln (+32 per key block), chunk 2*ks+g, i.e. slot (2*ks+g) ^ swz(ln) = 2*(ks ^ kx) + kg
   const int kx = swz<D>(ln) >> 1, kbase = ln * D + ((g ^ (swz<D>(ln) & 1)) << 3);
-  int vofs[2][NDB];  // V^T transpose read: rows 8*half + trow (+16 per step), 32 dims per block
+  int vofs[2][NDB];  // V^T transpose read: rows 8*half + trow (+16 per k-step), 32 dims per block
   {
     const int trow = 4 * g + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -213,30 +191,31 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
       }
   }
 
-  // class of tile t for row block rb: FULL (no mask needed) or PARTIAL (element
-  // mask).  A tile with no allowed pair is computed as PARTIAL (all of it
+  // wave-level class of tile t: FULL (no mask needed) or PARTIAL (element mask).
+  // A tile with no allowed pair for this wave is computed as PARTIAL (all of it
   // masked): that keeps the loop one straight pipeline, and such tiles are the
-  // few past each block's diagonal.
-  auto classify = [&](int t, int rb) {
+  // few past each wave's diagonal.
+  auto classify = [&](int t) {
     const int j0 = tile_of(t) * BK;
-    if (!blk_live[rb] || j0 + BK > p.Sk) return (int)kPartial;
+    if (!wave_live || j0 + BK > p.Sk) return (int)kPartial;
     if (!p.causal) return (int)kFull;
     int kmn, kmx;
     seg_range(p.ks, j0, j0 + BK, kmn, kmx);
-    return kmx <= qmin_b[rb] ? (int)kFull : (int)kPartial;
+    return kmx <= qmin_w ? (int)kFull : (int)kPartial;
   };
 
-  // S^T = K Q^T of the tile in stage STAGE for every row block; each K operand
-  // read serves all row blocks
-  auto scores = [&](auto STAGE, f32x16 (&st)[RB]) {
+  // S^T = K Q^T of the tile in stage STAGE, one 32-key block per output;
+  // register r of block mb holds key 32*mb + 8*(r/4) + 4*g + r%4 of query ln
+  auto scores = [&](auto STAGE, f32x16 (&st)[NMB]) {
     constexpr int stage = decltype(STAGE)::value;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) st[rb] = f32x16{};
+    for (int mb = 0; mb < NMB; ++mb) {
+      st[mb] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[stage][kbase + ((ks ^ kx) << 4)]);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) st[rb] = mfma32(as_bf16x8(a), qf[rb][ks], st[rb]);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[stage][mb * 32 * D + kbase + ((ks ^ kx) << 4)]);
+        st[mb] = mfma32(as_bf16x8(a), qf[ks], st[mb]);
+      }
     }
   };
 
@@ -244,8 +223,7 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
 
   // one pipeline step: softmax and P V of tile t (scores in st_cur, stage STAGE)
   // interleaved with the scores of tile t+1 (into st_next, stage STAGE+1)
-  auto step = [&](auto STAGE, int t, f32x16 (&st_cur)[RB], int (&cls_cur)[RB], f32x16 (&st_next)[RB],
-                  int (&cls_next)[RB]) {
+  auto step = [&](auto STAGE, int t, f32x16 (&st_cur)[NMB], int& cls_cur, f32x16 (&st_next)[NMB], int& cls_next) {
     constexpr int stage = decltype(STAGE)::value;
     constexpr int nstage = (stage + 1) % NST, fstage = (stage + NST - 1) % NST;
     // tile t+1 resident for every wave; everyone is done with stage (t-1) % NST
@@ -253,65 +231,59 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
     issue_tile(std::integral_constant<int, fstage>{}, t + NST - 1);
     const int j0 = tile_of(t) * BK;
     const bool has_next = t + 1 < nt;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) cls_next[rb] = has_next ? classify(t + 1, rb) : (int)kFull;
+    cls_next = has_next ? classify(t + 1) : (int)kFull;
 
+    if (cls_cur == kPartial) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if (cls_cur[rb] == kPartial) {
+      for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          st_cur[rb][r] = in_window(kwin[rb], j) ? st_cur[rb][r] : NEG_INF;
+          const int j = j0 + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+          st_cur[mb][r] = in_window(kwin, j) ? st_cur[mb][r] : NEG_INF;
         }
-      }
-      float mx = NEG_INF;
+    }
+    float mx = NEG_INF;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st_cur[rb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (__any(mx > m_run[rb] + raise_thr)) {
-        const float mnew = fmaxf(m_run[rb], mx);
-        const float alpha = (m_run[rb] == NEG_INF) ? 0.f : fast_exp2((m_run[rb] - mnew) * p.c);
-        l_run[rb] *= alpha;
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[rb][db] *= alpha;
-        m_run[rb] = mnew;
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st_cur[mb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_run + raise_thr)) {
+      const float mnew = fmaxf(m_run, mx);
+      const float alpha = (m_run == NEG_INF) ? 0.f : fast_exp2((m_run - mnew) * p.c);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      m_run = mnew;
     }
 
     // One straight-line block: the scores of tile t+1 (matrix cores) do not
     // depend on the softmax of tile t (vector ALUs), so the two interleave.  On
     // the last tile the scores of a dummy tile are computed and dropped.
     scores(std::integral_constant<int, nstage>{}, st_next);
-    bf16x8 pb0[RB], pb1[RB];
+    const float msub = (m_run == NEG_INF) ? 0.f : m_run * p.c;
+    bf16x8 pb[2 * NMB];  // P^T as B operands, one per 16-key k-step
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float msub = (m_run[rb] == NEG_INF) ? 0.f : m_run[rb] * p.c;
+    for (int mb = 0; mb < NMB; ++mb) {
       float e[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        e[r] = fast_exp2(__builtin_fmaf(st_cur[rb][r], p.c, -msub));
-        l_run[rb] += e[r];
+        e[r] = fast_exp2(__builtin_fmaf(st_cur[mb][r], p.c, -msub));
+        l_run += e[r];
       }
-      pb0[rb] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-      pb1[rb] = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+      pb[2 * mb] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      pb[2 * mb + 1] = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
     }
-    // O^T += V^T P^T; V^T read transposed from the row-major V tile, each read
-    // serving all row blocks
+    // O^T += V^T P^T; V^T read transposed from the row-major V tile
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const u32x2 lo0 = ds_read_tr16(&Vs[stage][vofs[0][db]]);
-      const u32x2 hi0 = ds_read_tr16(&Vs[stage][vofs[1][db]]);
-      const u32x2 lo1 = ds_read_tr16(&Vs[stage][vofs[0][db] + 16 * D]);
-      const u32x2 hi1 = ds_read_tr16(&Vs[stage][vofs[1][db] + 16 * D]);
-      const u32x4 a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
-      const u32x4 a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        oacc[rb][db] = mfma32(as_bf16x8(a0), pb0[rb], oacc[rb][db]);
-        oacc[rb][db] = mfma32(as_bf16x8(a1), pb1[rb], oacc[rb][db]);
+      for (int kk = 0; kk < 2 * NMB; ++kk) {
+        const u32x2 lo = ds_read_tr16(&Vs[stage][vofs[0][db] + 16 * kk * D]);
+        const u32x2 hi = ds_read_tr16(&Vs[stage][vofs[1][db] + 16 * kk * D]);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[db] = mfma32(as_bf16x8(a), pb[kk], oacc[db]);
       }
-    }
   };
 
   if (nt > 0) {
@@ -321,13 +293,8 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
     issue_tile(std::integral_constant<int, 1>{}, 1);
     issue_tile(std::integral_constant<int, 2>{}, 2);
     lds_ring_sync<(NST - 2) * LOADS_PER_TILE>();
-    int cls_a[RB], cls_b[RB];
-    f32x16 st_a[RB], st_b[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      cls_a[rb] = classify(0, rb);
-      cls_b[rb] = kFull;
-    }
+    int cls_a = classify(0), cls_b = kFull;
+    f32x16 st_a[NMB], st_b[NMB];
     scores(I0{}, st_a);
 
     // unrolled by the ring size so that every stage index is a constant and the
@@ -345,41 +312,37 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   }
 
   // ---- epilogue: normalise, write O and LSE
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const bool has = lt > 0.f;
+  const float inv = has ? 1.f / lt : 0.f;
+  if (p.o_bf16) {
+    uint16_t* op = static_cast<uint16_t*>(p.o) + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int qrow = r0w + 32 * rb + ln;
-    const float lt = l_run[rb] + __shfl_xor(l_run[rb], 32);
-    if (qrow >= p.Sq) continue;
-    const bool has = lt > 0.f;
-    const float inv = has ? 1.f / lt : 0.f;
-    if (p.o_bf16) {
-      uint16_t* op = static_cast<uint16_t*>(p.o) + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * g;
+        u32x2 val;
+        val[0] = pack_bf16x2(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv);
+        val[1] = pack_bf16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + d0) = val;
+      }
+  } else {
+    float* op = static_cast<float*>(p.o) + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = db * 32 + 8 * q4 + 4 * g;
-          u32x2 val;
-          val[0] = pack_bf16x2(oacc[rb][db][4 * q4 + 0] * inv, oacc[rb][db][4 * q4 + 1] * inv);
-          val[1] = pack_bf16x2(oacc[rb][db][4 * q4 + 2] * inv, oacc[rb][db][4 * q4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + d0) = val;
-        }
-    } else {
-      float* op = static_cast<float*>(p.o) + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = db * 32 + 8 * q4 + 4 * g;
-          f32x4 val = {oacc[rb][db][4 * q4 + 0] * inv, oacc[rb][db][4 * q4 + 1] * inv,
-                       oacc[rb][db][4 * q4 + 2] * inv, oacc[rb][db][4 * q4 + 3] * inv};
-          *reinterpret_cast<f32x4*>(op + d0) = val;
-        }
-    }
-    if (g == 0) {
-      const float lse = has ? (m_run[rb] * p.scale + logf(lt)) : NEG_INF;
-      p.lse[b * p.lse_bstride + (long)qrow * p.H + h] = lse;
-    }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * g;
+        f32x4 val = {oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv, oacc[db][4 * q4 + 2] * inv,
+                     oacc[db][4 * q4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(op + d0) = val;
+      }
+  }
+  if (g == 0) {
+    const float lse = has ? (m_run * p.scale + logf(lt)) : NEG_INF;
+    p.lse[b * p.lse_bstride + (long)qrow * p.H + h] = lse;
   }
 }
 
