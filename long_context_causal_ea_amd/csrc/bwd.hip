@@ -4,29 +4,30 @@
 //
 // Three launches on one stream:
 //  1. delta:  Delta_i = <dO_i, O_i>, one pass over O and dO (HBM-bound).
-//  2. dkdv:   one workgroup per 128-key block (4 waves x 32 keys, one wave per
-//             SIMD).  Each wave keeps its keys' K and V rows in registers and
-//             its dK^T, dV^T accumulators in fp32 registers, and streams 32-row
-//             query tiles (Q, dO, LSE, Delta) through a direct-to-LDS ring.
-//             Scores are computed with the key on the MFMA column (lane) axis,
-//             so P and dS come out of the MFMA already in the B-operand form
-//             that dV^T += dO^T P and dK^T += Q^T dS need; the dO^T and Q^T
-//             operands are read from the row-major tiles with the LDS
-//             transpose read.
-//  3. dq:     one workgroup per 128-query block, streaming key tiles like the
-//             forward; recomputes S^T and dP^T with the query on the lane axis
-//             and accumulates dQ^T += K^T dS^T in registers (K^T by transpose
-//             read of the row-major K tile).
+//  2. dkdv:   one workgroup per 128-key block: 8 waves, two per SIMD, in pairs
+//             sharing 32 keys (one wave holds K and produces P and dV, the
+//             other holds V and produces dS and dK; P crosses over in LDS).
+//             32-row query tiles (Q, dO, LSE, Delta) stream through a
+//             direct-to-LDS ring.  Scores are computed with the key on the MFMA
+//             column (lane) axis, so P and dS come out of the MFMA already in
+//             the B-operand form that dV^T += dO^T P and dK^T += Q^T dS need;
+//             the dO^T and Q^T operands are read from the row-major tiles with
+//             the LDS transpose read.
+//  3. dq:     one workgroup per 128-query block, streaming key/value tiles
+//             through a direct-to-LDS ring like the forward; recomputes S^T and
+//             dP^T with the query on the lane axis and accumulates
+//             dQ^T += K^T dS^T in registers (K^T by transpose read of the
+//             row-major K tile).
 // All LDS tiles are row-major with the XOR chunk swizzle of ea_device.h.
 // The dq pass recomputes the two score products instead of exchanging dS
-// through atomics: every output element is then written by exactly one
-// workgroup, without atomics, and results are bitwise reproducible.
+// through atomics (fp32 atomic adds into L2 were measured at about 1.4 TB/s on
+// MI355X, far too slow for the hundreds of GB of partial dQ a fused pass would
+// add): every output element is then written by exactly one workgroup and
+// results are bitwise reproducible.
 #include <type_traits>
 
 #include "ea_device.h"
 #include "ea_launch.h"
-
-// Tile and occupancy choices (workgroups per CU the register budget is sized for).
 
 namespace ea {
 
