@@ -19,6 +19,9 @@ nothing else).  Sources for the method:
   tokens across ranks).
 * EasyContext "1M tokens with minimal resources" page (cn486.com), usage code
   (each rank receives its local shard together with its local position ids).
+* The fused cross-entropy with in-place backward that the training step uses
+  (hotelren.com page, section on combining further optimisations; mlqm.cn
+  walkthrough, opening summary of the technology stack): ``xent.py``.
 
 Where the pages are silent (no formula, layout or mask rule is printed on any
 of them) the reading taken is stated next to the function that uses it.
@@ -31,3 +34,4 @@ from .attention import (  # noqa: F401
     allowed_mask, allowed_sums, attn_fwd, attn_bwd, lse_merge, attn_fwd_heads, attn_bwd_heads,
 )
 from .zigzag import zigzag_positions, ring_source, chunk_positions  # noqa: F401
+from .xent import xent_fwd_bwd  # noqa: F401

@@ -12,8 +12,10 @@ import pytest
 
 import oracle
 from oracle import attention as A
+from oracle import xent as X
 from oracle import zigzag as Z
 from tests import test_oracle as T
+from tests import test_oracle_xent as TX
 
 MUTANTS = {
     "strict_causal": ("pos_k[None, :] <= pos_q[:, None]", "pos_k[None, :] < pos_q[:, None]"),
@@ -36,6 +38,23 @@ ZMUTANTS = {
     "zigzag_swapped_order": ("[chunk_positions(rank, C), chunk_positions(2 * world - 1 - rank, C)]",
                              "[chunk_positions(2 * world - 1 - rank, C), chunk_positions(rank, C)]"),
 }
+
+XMUTANTS = {
+    "xent_no_onehot": ("grad[rows[keep], y[keep]] -= 1.0", "grad[rows[keep], y[keep]] -= 0.0"),
+    "xent_log2_lse": ("lse = m + np.log(np.exp(x - m[:, None]).sum(axis=1))",
+                      "lse = m + np.log2(np.exp(x - m[:, None]).sum(axis=1))"),
+    "xent_no_scale": ("grad *= grad_scale", "grad *= 1.0"),
+    "xent_ignored_kept": ("grad[~keep] = 0.0", "grad[~keep] = grad[~keep]"),
+    "xent_label_off_by_one": ("picked = np.where(keep, x[rows, np.where(keep, y, 0)], 0.0)",
+                              "picked = np.where(keep, x[rows, np.where(keep, (y + 1) % v, 0)], 0.0)"),
+}
+
+XPINS = [
+    TX.test_golden_two_classes,
+    lambda: TX.test_matches_torch_cross_entropy(0, 7, 5),
+    TX.test_uniform_logits_closed_form,
+    TX.test_invariants,
+]
 
 PINS = [
     lambda: T.test_golden_attention("causal_two_tokens.json"),
@@ -88,5 +107,12 @@ def test_zigzag_mutant_is_caught(name, monkeypatch):
     assert _fails(ZPINS) >= 1, f"no pin caught mutant {name}"
 
 
+@pytest.mark.parametrize("name", sorted(XMUTANTS))
+def test_xent_mutant_is_caught(name, monkeypatch):
+    mod = _load_mutant(X, *XMUTANTS[name])
+    monkeypatch.setattr(TX, "xent_fwd_bwd", mod.xent_fwd_bwd)
+    assert _fails(XPINS) >= 1, f"no pin caught mutant {name}"
+
+
 def test_unmutated_oracle_passes_all_pins():
-    assert _fails(PINS + ZPINS) == 0
+    assert _fails(PINS + ZPINS + XPINS) == 0
