@@ -133,6 +133,30 @@ int ea_lse_merge(float* o_acc, float* lse_acc, const void* o_part, int part_dtyp
                  int64_t q_batch_rows, void* stream);
 
 /*
+ * Fused cross-entropy over vocabulary logits, forward and backward, with the
+ * gradient written in place over the logits (the fused cross-entropy kernel
+ * with in-place backward of the training step: hotelren.com page, section on
+ * combining further optimisations; mlqm.cn walkthrough, summary of the
+ * technology stack).  For every row i of logits [rows, vocab] (row i starts at
+ * element i * row_stride) with label y_i:
+ *   lse_i  = ln sum_j exp(x_ij)                         (fp32 [rows])
+ *   loss_i = lse_i - x_{i,y_i}                          (fp32 [rows])
+ *   x_ij  <- grad_scale * (exp(x_ij - lse_i) - [j == y_i])
+ * Rows with y_i == ignore_index get loss 0 and gradient 0 (lse is still
+ * written).  Any other label outside [0, vocab) gives loss NaN and a NaN
+ * gradient row.  logits are bf16 or fp32 (dtype EA_BF16 / EA_F32; the gradient
+ * is rounded to nearest even into bf16); labels are int64 on the device.  For a
+ * mean over the rows that are not ignored pass grad_scale = 1 / that count.
+ * Alignment: logits to their element size (any row_stride; rows that start
+ * on 16 bytes are read and written in 16-byte pieces only), labels 8, loss and
+ * lse 4.  Sizes: 0 <= rows < 2^31, 1 <= vocab <= row_stride,
+ * vocab < 2^31.  loss, lse and labels must not overlap the logits or each
+ * other.  rows == 0 does nothing.  Enqueued on `stream` like the calls above.
+ */
+int ea_xent_fwd_bwd(void* logits, int dtype, const int64_t* labels, float* loss, float* lse, int64_t rows,
+                    int64_t vocab, int64_t row_stride, int64_t ignore_index, float grad_scale, void* stream);
+
+/*
  * Host-only helper (no HIP call): position segments of one rank's share in a
  * zigzag ring.  The sequence of s_total tokens is cut into 2*world equal
  * chunks of C tokens; rank r holds chunk r followed by chunk 2*world-1-r
@@ -167,7 +191,8 @@ enum ea_kernel {
   EA_KERNEL_BWD_DKDV = 2,
   EA_KERNEL_BWD_DQ = 3,
   EA_KERNEL_LSE_MERGE = 4,
-  EA_KERNEL_COUNT = 5
+  EA_KERNEL_XENT = 5,
+  EA_KERNEL_COUNT = 6
 };
 int ea_profile_begin(void);
 int ea_profile_end(void);

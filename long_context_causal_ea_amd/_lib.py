@@ -47,6 +47,8 @@ def lib():
     L.ea_attn_bwd.restype = i32
     L.ea_lse_merge.argtypes = [vp, vp, vp, i32, vp, i32, i32, i64, i32, i64, vp]
     L.ea_lse_merge.restype = i32
+    L.ea_xent_fwd_bwd.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, i64, f32, vp]
+    L.ea_xent_fwd_bwd.restype = i32
     L.ea_zigzag_segments.argtypes = [i64, i32, i32, pi64]
     L.ea_zigzag_segments.restype = i32
     L.ea_ring_source.argtypes = [i32, i32, i32]
@@ -69,11 +71,11 @@ def lib():
     return L
 
 
-EXPORTS = ("ea_attn_fwd", "ea_attn_bwd", "ea_lse_merge", "ea_zigzag_segments", "ea_ring_source",
+EXPORTS = ("ea_attn_fwd", "ea_attn_bwd", "ea_lse_merge", "ea_xent_fwd_bwd", "ea_zigzag_segments", "ea_ring_source",
            "ea_strerror", "ea_last_hip_error", "ea_version", "ea_profile_begin", "ea_profile_end",
            "ea_profile_query", "ea_kernel_name")
 
-KERNELS = ("fwd", "bwd_delta", "bwd_dkdv", "bwd_dq", "lse_merge")
+KERNELS = ("fwd", "bwd_delta", "bwd_dkdv", "bwd_dq", "lse_merge", "xent")
 
 
 def strerror(status: int) -> str:
@@ -193,6 +195,22 @@ def ea_lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
     st = lib().ea_lse_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _dtype_code(o_part), _ptr(lse_part),
                             B, H, sq, D, qbr, _stream(stream))
     _check(st, "ea_lse_merge")
+
+
+def ea_xent_fwd_bwd(logits, labels, loss, lse, grad_scale=1.0, ignore_index=-100, stream=None):
+    """Cross-entropy of each row of logits [rows, vocab] (bf16 or fp32, rows contiguous) against int64
+    labels [rows]; writes loss and lse (fp32 [rows]) and overwrites logits with the gradient."""
+    import torch
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [rows, vocab] with contiguous rows")
+    rows, vocab = logits.shape
+    row_stride = logits.stride(0) if rows > 1 else vocab
+    for t, dt, name in ((labels, torch.int64, "labels"), (loss, torch.float32, "loss"), (lse, torch.float32, "lse")):
+        if t.dtype != dt or t.dim() != 1 or t.shape[0] != rows or (rows > 1 and t.stride(0) != 1):
+            raise ValueError(f"{name} must be a contiguous {dt} vector of {rows} rows")
+    st = lib().ea_xent_fwd_bwd(_ptr(logits), _dtype_code(logits), _ptr(labels), _ptr(loss), _ptr(lse), rows,
+                               vocab, row_stride, int(ignore_index), float(grad_scale), _stream(stream))
+    _check(st, "ea_xent_fwd_bwd")
 
 
 def ea_zigzag_segments(s_total: int, world: int, rank: int):

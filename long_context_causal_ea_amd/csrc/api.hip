@@ -130,7 +130,7 @@ const char* ea_strerror(int status) {
     case EA_ERR_SHAPE: return "B, H, sequence length or batch row stride out of range";
     case EA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype, mask mode or scale";
     case EA_ERR_POSITIONS: return "bad position segments (count, lengths, starts, or a position >= 2^31)";
-    case EA_ERR_ALIGN: return "pointer misaligned (bf16 tensors and outputs need 16 bytes, fp32 rows 4)";
+    case EA_ERR_ALIGN: return "pointer misaligned (the alignment each call documents in ea_attn.h)";
     case EA_ERR_ALIAS: return "an output buffer overlaps an input buffer";
     case EA_ERR_HIP: return "a HIP launch failed (see ea_last_hip_error)";
     default: return "unknown status";
@@ -184,6 +184,7 @@ const char* ea_kernel_name(int kernel) {
     case EA_KERNEL_BWD_DKDV: return "bwd_dkdv";
     case EA_KERNEL_BWD_DQ: return "bwd_dq";
     case EA_KERNEL_LSE_MERGE: return "lse_merge";
+    case EA_KERNEL_XENT: return "xent";
     default: return "unknown";
   }
 }
@@ -344,6 +345,38 @@ int ea_lse_merge(float* o_acc, float* lse_acc, const void* o_part, int part_dtyp
   a.q_batch_rows = q_batch_rows;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = timed_launch(EA_KERNEL_LSE_MERGE, s, [&] { return ea::launch_merge(a, s); });
+  return e == hipSuccess ? EA_OK : hip_fail(e);
+}
+
+int ea_xent_fwd_bwd(void* logits, int dtype, const int64_t* labels, float* loss, float* lse, int64_t rows,
+                    int64_t vocab, int64_t row_stride, int64_t ignore_index, float grad_scale, void* stream) {
+  if (rows < 0 || rows >= kPosLimit || vocab < 1 || vocab >= kPosLimit || row_stride < vocab) return EA_ERR_SHAPE;
+  if (dtype != EA_F32 && dtype != EA_BF16) return EA_ERR_UNSUPPORTED;
+  if (!isfinite(grad_scale)) return EA_ERR_UNSUPPORTED;
+  if (rows == 0) return EA_OK;
+  if (!logits || !labels || !loss || !lse) return EA_ERR_NULL;
+  const int esz = dtype == EA_F32 ? 4 : 2;
+  if (!aligned(logits, esz) || !aligned(labels, 8) || !aligned(loss, 4) || !aligned(lse, 4))
+    return EA_ERR_ALIGN;
+  const Span sx = Span{(uintptr_t)logits, (uintptr_t)logits + (uintptr_t)(((rows - 1) * row_stride + vocab) * esz)};
+  const Span sy = Span{(uintptr_t)labels, (uintptr_t)labels + (uintptr_t)(rows * 8)};
+  const Span sl = Span{(uintptr_t)loss, (uintptr_t)loss + (uintptr_t)(rows * 4)};
+  const Span se = Span{(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(rows * 4)};
+  if (overlap(sx, sy) || overlap(sx, sl) || overlap(sx, se) || overlap(sy, sl) || overlap(sy, se) || overlap(sl, se))
+    return EA_ERR_ALIAS;
+  ea::XentArgs a;
+  a.logits = logits;
+  a.labels = labels;
+  a.loss = loss;
+  a.lse = lse;
+  a.rows = (long)rows;
+  a.row_stride = (long)row_stride;
+  a.V = (int)vocab;
+  a.ignore_index = (long)ignore_index;
+  a.grad_scale = grad_scale;
+  a.bf16 = dtype == EA_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed_launch(EA_KERNEL_XENT, s, [&] { return ea::launch_xent(a, s); });
   return e == hipSuccess ? EA_OK : hip_fail(e);
 }
 

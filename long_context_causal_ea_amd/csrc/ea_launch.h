@@ -55,10 +55,23 @@ struct MergeArgs {
   int64_t q_batch_rows;
 };
 
+struct XentArgs {
+  void* logits;  // [rows, V] with row_stride, overwritten by the gradient
+  const int64_t* labels;
+  float* loss;
+  float* lse;
+  long rows, row_stride;
+  int V;
+  long ignore_index;
+  float grad_scale;
+  int bf16;
+};
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_xent(const XentArgs& a, hipStream_t stream);
 
 }  // namespace ea

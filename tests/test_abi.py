@@ -131,6 +131,32 @@ def test_merge_empty_is_noop():
     assert _merge(Sq=0, qbr=0, oa=0, la=0, op=0, lp=0) == OK
 
 
+def _xent(**kw):
+    a = dict(x=P, dt=1, y=P + STEP, loss=P + 2 * STEP, lse=P + 3 * STEP, rows=4, V=32000, rs=32000, ign=-100,
+             g=0.25)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return ea.lib().ea_xent_fwd_bwd(vp(a["x"]), a["dt"], vp(a["y"]), vp(a["loss"]), vp(a["lse"]), a["rows"], a["V"],
+                                    a["rs"], a["ign"], a["g"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), NULL), (dict(y=0), NULL), (dict(loss=0), NULL), (dict(lse=0), NULL),
+    (dict(rows=-1), SHAPE), (dict(V=0), SHAPE), (dict(rs=31999), SHAPE), (dict(rows=1 << 31), SHAPE),
+    (dict(dt=2), UNSUP), (dict(g=float("inf")), UNSUP), (dict(g=float("nan")), UNSUP),
+    (dict(x=P + 1), ALIGN), (dict(dt=0, x=P + 2), ALIGN), (dict(y=P + STEP + 4), ALIGN),
+    (dict(loss=P + 2 * STEP + 2), ALIGN),
+    (dict(y=P + 64), ALIAS), (dict(loss=P), ALIAS), (dict(lse=P + 2 * STEP + 8), ALIAS),
+    (dict(lse=P + STEP + 16), ALIAS),
+])
+def test_xent_rejects_bad_arguments(kw, code):
+    assert _xent(**kw) == code
+
+
+def test_xent_empty_is_noop():
+    assert _xent(rows=0, x=0, y=0, loss=0, lse=0) == OK
+
+
 @pytest.mark.parametrize("W", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("C", [1, 5, 37, 32768, 43750])
 def test_zigzag_segments_match_oracle_positions(W, C):
