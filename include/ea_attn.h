@@ -135,9 +135,9 @@ int ea_lse_merge(float* o_acc, float* lse_acc, const void* o_part, int part_dtyp
 /*
  * Fused cross-entropy over vocabulary logits, forward and backward, with the
  * gradient written in place over the logits (the fused cross-entropy kernel
- * with in-place backward of the training step: hotelren.com page, section on
- * combining further optimisations; mlqm.cn walkthrough, summary of the
- * technology stack).  For every row i of logits [rows, vocab] (row i starts at
+ * with in-place backward of the training step: kwkr.cn ZeRO-3 offload page,
+ * section on advanced optimisation combined with other techniques, item 1;
+ * cn486.com page, summary of the training script's technology stack).  For every row i of logits [rows, vocab] (row i starts at
  * element i * row_stride) with label y_i:
  *   lse_i  = ln sum_j exp(x_ij)                         (fp32 [rows])
  *   loss_i = lse_i - x_{i,y_i}                          (fp32 [rows])

@@ -1,8 +1,8 @@
 // Fused cross-entropy forward + backward over vocabulary logits, gradient
 // written in place (the fused cross-entropy kernel with in-place backward that
-// the training step uses: EasyContext core-technology page, hotelren.com,
-// section on combining further optimisations; mlqm.cn walkthrough, opening
-// summary of the technology stack).
+// the training step uses: EasyContext ZeRO-3 offload page, kwkr.cn, section
+// on advanced optimisation combined with other techniques, item 1; cn486.com
+// page, summary of the training script's technology stack).
 //
 // Per row i of x [N, V] with label y_i and upstream gradient scale g:
 //   LSE_i = ln sum_j exp(x_ij),   loss_i = LSE_i - x_{i,y_i},

@@ -20,8 +20,9 @@ nothing else).  Sources for the method:
 * EasyContext "1M tokens with minimal resources" page (cn486.com), usage code
   (each rank receives its local shard together with its local position ids).
 * The fused cross-entropy with in-place backward that the training step uses
-  (hotelren.com page, section on combining further optimisations; mlqm.cn
-  walkthrough, opening summary of the technology stack): ``xent.py``.
+  (EasyContext ZeRO-3 offload page, kwkr.cn, section on advanced optimisation
+  combined with other techniques, item 1; cn486.com page, the summary of the
+  training script's technology stack): ``xent.py``.
 
 Where the pages are silent (no formula, layout or mask rule is printed on any
 of them) the reading taken is stated next to the function that uses it.

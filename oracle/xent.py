@@ -4,9 +4,10 @@ TEST INFRASTRUCTURE ONLY (see the package header).
 
 The training script the pages walk through computes its language-model loss
 with FlashAttention's fused cross-entropy kernel, backward done in place over
-the logits (EasyContext core-technology page, hotelren.com, section on further
-optimisation combined with other techniques; EasyContext 200-line training
-script walkthrough, mlqm.cn, opening summary of the technology stack).  No
+the logits (EasyContext memory-optimisation page on DeepSpeed ZeRO-3 offload,
+kwkr.cn, section on advanced optimisation combined with other techniques, item
+1; EasyContext "1M tokens with minimal resources" page, cn486.com, the summary
+of the training script's technology stack).  No
 formula is printed; this is the textbook definition, per row i of a [N, V]
 logit matrix x with integer label y_i:
 
