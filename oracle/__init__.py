@@ -23,6 +23,10 @@ nothing else).  Sources for the method:
   (EasyContext ZeRO-3 offload page, kwkr.cn, section on advanced optimisation
   combined with other techniques, item 1; cn486.com page, the summary of the
   training script's technology stack): ``xent.py``.
+* The rotary position embedding whose base the pages raise for long contexts
+  (hotelren.com page, further optimisations; mlqm.cn walkthrough, the
+  rope-theta option; kwkr.cn page, training script and advanced optimisation
+  item 2; cn486.com page, training strategy): ``rope.py``.
 
 Where the pages are silent (no formula, layout or mask rule is printed on any
 of them) the reading taken is stated next to the function that uses it.
@@ -36,3 +40,4 @@ from .attention import (  # noqa: F401
 )
 from .zigzag import zigzag_positions, ring_source, chunk_positions  # noqa: F401
 from .xent import xent_fwd_bwd  # noqa: F401
+from .rope import rope, round_bf16, attn_bwd_rope  # noqa: F401

@@ -12,9 +12,11 @@ import pytest
 
 import oracle
 from oracle import attention as A
+from oracle import rope as R
 from oracle import xent as X
 from oracle import zigzag as Z
 from tests import test_oracle as T
+from tests import test_oracle_rope as TR
 from tests import test_oracle_xent as TX
 
 MUTANTS = {
@@ -56,6 +58,30 @@ XPINS = [
     TX.test_invariants,
 ]
 
+RMUTANTS = {
+    "rope_sin_sign": ("return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)",
+                      "return np.concatenate([a * c + b * s, b * c - a * s], axis=-1)"),
+    "rope_interleaved_pairs": ("a, b = x[..., :half], x[..., half:]", "a, b = x[..., 0::2], x[..., 1::2]"),
+    "rope_exponent_k_over_d": ("-2.0 * k / D", "-1.0 * k / D"),
+    "rope_inverse_not_transposed": ("s = -s", "s = s"),
+    "rope_position_off_by_one": ("phi = pos.astype(np.float64)[:, None]", "phi = (pos + 1).astype(np.float64)[:, None]"),
+    "bf16_truncates": ("r = (bits + half_ulp + lsb) &", "r = (bits) &"),
+    "rope_dq_not_rotated_back": ('out["dq"] = rope(out["dq"][:, None, :], pos_q, theta, inverse=True)[:, 0, :]',
+                                 'out["dq"] = out["dq"]'),
+    "rope_dk_rotated_forward": ('out["dk"] = rope(out["dk"][:, None, :], pos_k, theta, inverse=True)[:, 0, :]',
+                                'out["dk"] = rope(out["dk"][:, None, :], pos_k, theta)[:, 0, :]'),
+}
+
+RPINS = [
+    TR.test_golden_quarter_turn,
+    TR.test_d2_is_complex_rotation,
+    lambda: TR.test_matches_transformers_llama(64, 1e4),
+    TR.test_orthogonal_and_inverse,
+    TR.test_inv_freq_closed_form,
+    TR.test_round_bf16_against_torch_and_ties,
+    TR.test_attention_gradient_through_rotation,
+]
+
 PINS = [
     lambda: T.test_golden_attention("causal_two_tokens.json"),
     lambda: T.test_golden_attention("full_one_query.json"),
@@ -77,6 +103,7 @@ def _load_mutant(module, old, new):
     src = inspect.getsource(module)
     assert src.count(old) == 1, old
     mod = types.ModuleType(module.__name__ + "_mutant")
+    mod.__package__ = module.__package__  # relative imports of the oracle package
     exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
     return mod
 
@@ -114,5 +141,13 @@ def test_xent_mutant_is_caught(name, monkeypatch):
     assert _fails(XPINS) >= 1, f"no pin caught mutant {name}"
 
 
+@pytest.mark.parametrize("name", sorted(RMUTANTS))
+def test_rope_mutant_is_caught(name, monkeypatch):
+    mod = _load_mutant(R, *RMUTANTS[name])
+    for fn in ("rope", "round_bf16", "attn_bwd_rope", "inv_freq"):
+        monkeypatch.setattr(TR, fn, getattr(mod, fn))
+    assert _fails(RPINS) >= 1, f"no pin caught mutant {name}"
+
+
 def test_unmutated_oracle_passes_all_pins():
-    assert _fails(PINS + ZPINS + XPINS) == 0
+    assert _fails(PINS + ZPINS + XPINS + RPINS) == 0
