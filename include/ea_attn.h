@@ -157,6 +157,27 @@ int ea_xent_fwd_bwd(void* logits, int dtype, const int64_t* labels, float* loss,
                     int64_t vocab, int64_t row_stride, int64_t ignore_index, float grad_scale, void* stream);
 
 /*
+ * Rotary position embedding by global position (the rotary base that the
+ * pages raise for long contexts: hotelren.com page, further optimisations;
+ * kwkr.cn ZeRO-3 offload page, training script rope-theta and advanced
+ * optimisation item 2; cn486.com page, training strategy).  Llama
+ * "rotate-half" convention: for each row of x [B, S, H, D] at position p (from
+ * seg, as for ea_attn_fwd) and k = 0 .. D/2-1, with phi = p * theta^(-2k/D),
+ *   y_k       = x_k cos(phi) - x_{k+D/2} sin(phi)
+ *   y_{k+D/2} = x_{k+D/2} cos(phi) + x_k sin(phi)
+ * inverse = 1 applies the transpose (phi -> -phi): it turns the gradient with
+ * respect to rotated rows into the gradient with respect to the unrotated ones
+ * (dQ, dK of ea_attn_bwd on rotated Q, K).  Angles are formed in fp64 (exact
+ * for positions up to 2^31), the rotation in fp32, one rounding to the output.
+ * x and y: dtype EA_BF16 or EA_F32 (both), same layout and batch stride
+ * batch_rows * H * D elements, 16-byte aligned; y == x rotates in place,
+ * otherwise they must not overlap.  D in {64, 128}; 0 < theta finite.
+ * S == 0 does nothing.  Enqueued on `stream` like the calls above.
+ */
+int ea_rope(const void* x, void* y, int dtype, int B, int H, int64_t S, int D, int64_t batch_rows,
+            const int64_t* seg, int n_seg, double theta, int inverse, void* stream);
+
+/*
  * Host-only helper (no HIP call): position segments of one rank's share in a
  * zigzag ring.  The sequence of s_total tokens is cut into 2*world equal
  * chunks of C tokens; rank r holds chunk r followed by chunk 2*world-1-r
@@ -192,7 +213,8 @@ enum ea_kernel {
   EA_KERNEL_BWD_DQ = 3,
   EA_KERNEL_LSE_MERGE = 4,
   EA_KERNEL_XENT = 5,
-  EA_KERNEL_COUNT = 6
+  EA_KERNEL_ROPE = 6,
+  EA_KERNEL_COUNT = 7
 };
 int ea_profile_begin(void);
 int ea_profile_end(void);

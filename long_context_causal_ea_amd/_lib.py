@@ -49,6 +49,8 @@ def lib():
     L.ea_lse_merge.restype = i32
     L.ea_xent_fwd_bwd.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, i64, f32, vp]
     L.ea_xent_fwd_bwd.restype = i32
+    L.ea_rope.argtypes = [vp, vp, i32, i32, i32, i64, i32, i64, pi64, i32, ctypes.c_double, i32, vp]
+    L.ea_rope.restype = i32
     L.ea_zigzag_segments.argtypes = [i64, i32, i32, pi64]
     L.ea_zigzag_segments.restype = i32
     L.ea_ring_source.argtypes = [i32, i32, i32]
@@ -71,11 +73,12 @@ def lib():
     return L
 
 
-EXPORTS = ("ea_attn_fwd", "ea_attn_bwd", "ea_lse_merge", "ea_xent_fwd_bwd", "ea_zigzag_segments", "ea_ring_source",
+EXPORTS = ("ea_attn_fwd", "ea_attn_bwd", "ea_lse_merge", "ea_xent_fwd_bwd", "ea_rope", "ea_zigzag_segments",
+           "ea_ring_source",
            "ea_strerror", "ea_last_hip_error", "ea_version", "ea_profile_begin", "ea_profile_end",
            "ea_profile_query", "ea_kernel_name")
 
-KERNELS = ("fwd", "bwd_delta", "bwd_dkdv", "bwd_dq", "lse_merge", "xent")
+KERNELS = ("fwd", "bwd_delta", "bwd_dkdv", "bwd_dq", "lse_merge", "xent", "rope")
 
 
 def strerror(status: int) -> str:
@@ -211,6 +214,21 @@ def ea_xent_fwd_bwd(logits, labels, loss, lse, grad_scale=1.0, ignore_index=-100
     st = lib().ea_xent_fwd_bwd(_ptr(logits), _dtype_code(logits), _ptr(labels), _ptr(loss), _ptr(lse), rows,
                                vocab, row_stride, int(ignore_index), float(grad_scale), _stream(stream))
     _check(st, "ea_xent_fwd_bwd")
+
+
+def ea_rope(x, y, seg, theta, inverse=False, stream=None):
+    """Rotary embedding of x [B, S, H, D] (bf16 or fp32) by the positions of seg into y (same shape, dtype and
+    batch stride; y may be x).  inverse=True applies the transpose (for gradients)."""
+    if x.dim() != 4 or y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("x and y must be [B, S, H, D] tensors of one shape and dtype")
+    B, S, H, D = x.shape
+    rows = _rows(x, H, D)
+    if _rows(y, H, D) != rows:
+        raise ValueError("x and y must have the same batch stride")
+    sg, ns = _segs(seg)
+    st = lib().ea_rope(_ptr(x), _ptr(y), _dtype_code(x), B, H, S, D, rows, sg, ns, float(theta), int(bool(inverse)),
+                       _stream(stream))
+    _check(st, "ea_rope")
 
 
 def ea_zigzag_segments(s_total: int, world: int, rank: int):

@@ -25,7 +25,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-variable", "-Wno-unused-function",
 ]
 
-SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "merge.hip", "xent.hip"]
+SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "merge.hip", "xent.hip", "rope.hip"]
 
 
 def _compile(src: str, obj_dir: str) -> str:

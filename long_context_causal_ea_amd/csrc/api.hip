@@ -185,6 +185,7 @@ const char* ea_kernel_name(int kernel) {
     case EA_KERNEL_BWD_DQ: return "bwd_dq";
     case EA_KERNEL_LSE_MERGE: return "lse_merge";
     case EA_KERNEL_XENT: return "xent";
+    case EA_KERNEL_ROPE: return "rope";
     default: return "unknown";
   }
 }
@@ -377,6 +378,38 @@ int ea_xent_fwd_bwd(void* logits, int dtype, const int64_t* labels, float* loss,
   a.bf16 = dtype == EA_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = timed_launch(EA_KERNEL_XENT, s, [&] { return ea::launch_xent(a, s); });
+  return e == hipSuccess ? EA_OK : hip_fail(e);
+}
+
+int ea_rope(const void* x, void* y, int dtype, int B, int H, int64_t S, int D, int64_t batch_rows,
+            const int64_t* seg, int n_seg, double theta, int inverse, void* stream) {
+  if (B < 1 || H < 1 || S < 0 || S >= kPosLimit || batch_rows < S || batch_rows >= kPosLimit) return EA_ERR_SHAPE;
+  if ((int64_t)B * S >= kPosLimit) return EA_ERR_SHAPE;
+  if (D != 64 && D != 128) return EA_ERR_UNSUPPORTED;
+  if (dtype != EA_F32 && dtype != EA_BF16) return EA_ERR_UNSUPPORTED;
+  if (!(theta > 0.0) || !isfinite(theta)) return EA_ERR_UNSUPPORTED;
+  if (inverse != 0 && inverse != 1) return EA_ERR_UNSUPPORTED;
+  ea::RopeArgs a;
+  int st = check_segs(seg, n_seg, S, &a.seg);
+  if (st) return st;
+  if (S == 0) return EA_OK;
+  if (!x || !y) return EA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return EA_ERR_ALIGN;
+  const int esz = dtype == EA_F32 ? 4 : 2;
+  const Span sx = span_of(x, B, batch_rows, S, (int64_t)H * D, esz), sy = span_of(y, B, batch_rows, S, (int64_t)H * D, esz);
+  if (x != y && overlap(sx, sy)) return EA_ERR_ALIAS;
+  a.x = x;
+  a.y = y;
+  a.B = B;
+  a.H = H;
+  a.S = (int)S;
+  a.D = D;
+  a.batch_rows = batch_rows;
+  a.inverse = inverse;
+  a.bf16 = dtype == EA_BF16;
+  for (int k = 0; k < 64; ++k) a.inv_freq[k] = k < D / 2 ? pow(theta, -2.0 * k / D) : 0.0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed_launch(EA_KERNEL_ROPE, s, [&] { return ea::launch_rope(a, s); });
   return e == hipSuccess ? EA_OK : hip_fail(e);
 }
 

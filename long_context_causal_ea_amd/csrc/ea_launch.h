@@ -67,11 +67,23 @@ struct XentArgs {
   int bf16;
 };
 
+struct RopeArgs {
+  const void* x;  // [B, S, H, D] with batch stride batch_rows * H * D
+  void* y;        // same layout; may equal x
+  int B, H, S, D;
+  int64_t batch_rows;
+  SegArg seg;
+  int inverse;
+  int bf16;
+  double inv_freq[64];  // theta^(-2k/D), k < D/2
+};
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_xent(const XentArgs& a, hipStream_t stream);
+hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 
 }  // namespace ea

@@ -13,6 +13,11 @@ rule on global positions selects, per step, the full, causal or half blocks.
 ``DenseCausal`` is the whole-sequence case: one forward and one backward
 call over positions 0..S-1.
 
+With ``rope_theta`` set, both drivers take unrotated Q and K: the forward first
+rotates them by their global positions (``ea_rope`` into buffers the driver
+owns) and the backward rotates dQ and dK back (the transpose, in place), so the
+gradients are with respect to the unrotated inputs.
+
 All buffers are allocated when the driver is built; ``forward`` and
 ``backward`` enqueue work on the current stream and allocate nothing.
 """
@@ -22,9 +27,15 @@ from . import _lib as L
 
 
 class DenseCausal:
-    def __init__(self, q, k, v, causal=True, scale=None, o_dtype=torch.float32):
+    def __init__(self, q, k, v, causal=True, scale=None, o_dtype=torch.float32, rope_theta=None):
         B, S, H, D = q.shape
-        self.q, self.k, self.v = q, k, v
+        self.rope_theta = rope_theta
+        self.q_in, self.k_in = q, k
+        if rope_theta is None:
+            self.q, self.k = q, k
+        else:  # rotated copies, refreshed by every forward
+            self.q, self.k = torch.empty_like(q), torch.empty_like(k)
+        self.v = v
         self.causal = causal
         self.scale = D ** -0.5 if scale is None else scale
         dev = q.device
@@ -38,6 +49,9 @@ class DenseCausal:
         self.k_seg = [0, k.shape[1]]
 
     def forward(self, stream=None):
+        if self.rope_theta is not None:
+            L.ea_rope(self.q_in, self.q, self.q_seg, self.rope_theta, stream=stream)
+            L.ea_rope(self.k_in, self.k, self.k_seg, self.rope_theta, stream=stream)
         L.ea_attn_fwd(self.q, self.k, self.v, self.o, self.lse, self.q_seg, self.k_seg, self.causal, self.scale,
                       stream)
 
@@ -47,6 +61,9 @@ class DenseCausal:
         self.dv.zero_()
         L.ea_attn_bwd(self.q, self.k, self.v, self.o, do, self.lse, self.delta, self.dq, self.dk, self.dv,
                       self.q_seg, self.k_seg, self.causal, self.scale, delta_ready=False, stream=stream)
+        if self.rope_theta is not None:
+            L.ea_rope(self.dq, self.dq, self.q_seg, self.rope_theta, inverse=True, stream=stream)
+            L.ea_rope(self.dk, self.dk, self.k_seg, self.rope_theta, inverse=True, stream=stream)
 
     def step(self, do, stream=None):
         self.forward(stream)
@@ -61,11 +78,17 @@ class ZigzagRingRank:
            [2C*s, 2C*(s+1)) are rank s's local keys/values.
     """
 
-    def __init__(self, q, k, v, world, rank, scale=None):
+    def __init__(self, q, k, v, world, rank, scale=None, rope_theta=None):
         B, sq, H, D = q.shape
         if sq % 2 or k.shape[1] != world * sq:
             raise ValueError("q must hold 2C rows and k/v W*2C rows")
-        self.q, self.k, self.v = q, k, v
+        self.rope_theta = rope_theta
+        self.q_in, self.k_in = q, k
+        if rope_theta is None:
+            self.q, self.k = q, k
+        else:
+            self.q, self.k = torch.empty_like(q), torch.empty_like(k)
+        self.v = v
         self.W, self.r = world, rank
         self.C = sq // 2
         self.s_total = world * sq
@@ -82,12 +105,25 @@ class ZigzagRingRank:
         self.q_seg = L.ea_zigzag_segments(self.s_total, world, rank)
         self.sources = [L.ea_ring_source(rank, t, world) for t in range(world)]
         self.k_segs = [L.ea_zigzag_segments(self.s_total, world, s) for s in self.sources]
+        self.share_segs = [L.ea_zigzag_segments(self.s_total, world, s) for s in range(world)]
+
+    def _share(self, s, x):
+        return x[:, 2 * self.C * s: 2 * self.C * (s + 1)]
+
+    def _rope_all(self, src_q, dst_q, src_k, dst_k, inverse, stream):
+        # each rank's share carries that rank's zigzag positions
+        L.ea_rope(src_q, dst_q, self.q_seg, self.rope_theta, inverse=inverse, stream=stream)
+        for s in range(self.W):
+            L.ea_rope(self._share(s, src_k), self._share(s, dst_k), self.share_segs[s], self.rope_theta,
+                      inverse=inverse, stream=stream)
 
     def _block(self, t, x):
         s = self.sources[t]
         return x[:, 2 * self.C * s: 2 * self.C * (s + 1)]
 
     def forward(self, stream=None):
+        if self.rope_theta is not None:
+            self._rope_all(self.q_in, self.q, self.k_in, self.k, False, stream)
         for t in range(self.W):
             kb, vb = self._block(t, self.k), self._block(t, self.v)
             if t == 0:
@@ -107,6 +143,8 @@ class ZigzagRingRank:
             L.ea_attn_bwd(self.q, kb, vb, self.o, do, self.lse, self.delta, self.dq, self._block(t, self.dk),
                           self._block(t, self.dv), self.q_seg, self.k_segs[t], True, self.scale,
                           delta_ready=(t > 0), stream=stream)
+        if self.rope_theta is not None:
+            self._rope_all(self.dq, self.dq, self.dk, self.dk, True, stream)
 
     def step(self, do, stream=None):
         self.forward(stream)

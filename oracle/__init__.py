@@ -40,4 +40,4 @@ from .attention import (  # noqa: F401
 )
 from .zigzag import zigzag_positions, ring_source, chunk_positions  # noqa: F401
 from .xent import xent_fwd_bwd  # noqa: F401
-from .rope import round_bf16, attn_bwd_rope  # noqa: F401  (oracle.rope stays the module; its rope() is oracle.rope.rope)
+from .rope import round_bf16, attn_bwd_rope, attn_bwd_rope_heads  # noqa: F401  (oracle.rope stays the module; its rope() is oracle.rope.rope)

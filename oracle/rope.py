@@ -26,7 +26,7 @@ the attention oracle, and rotate dQ and dK back.
 """
 import numpy as np
 
-from .attention import attn_bwd
+from .attention import _f64, attn_bwd
 
 
 def inv_freq(D: int, theta: float) -> np.ndarray:
@@ -39,7 +39,7 @@ def inv_freq(D: int, theta: float) -> np.ndarray:
 
 def rope(x, pos, theta: float, inverse: bool = False) -> np.ndarray:
     """Rotate x [..., S, H, D] (positions pos [S]) in fp64; inverse=True applies the transpose."""
-    x = np.asarray(x, dtype=np.float64)
+    x = _f64(x)
     pos = np.asarray(pos, dtype=np.int64)
     D = x.shape[-1]
     half = D // 2
@@ -79,10 +79,26 @@ def attn_bwd_rope(q, k, v, do, pos_q, pos_k, causal: bool, scale: float, theta: 
     Returns the dict of `attn_bwd` with dq and dk rotated back, plus the rotated
     bf16 inputs used ("q_rot", "k_rot").
     """
-    qr = round_bf16(rope(np.asarray(q, np.float64)[:, None, :], pos_q, theta)[:, 0, :])
-    kr = round_bf16(rope(np.asarray(k, np.float64)[:, None, :], pos_k, theta)[:, 0, :])
+    qr = round_bf16(rope(_f64(q)[:, None, :], pos_q, theta)[:, 0, :])
+    kr = round_bf16(rope(_f64(k)[:, None, :], pos_k, theta)[:, 0, :])
     out = attn_bwd(qr, kr, v, do, pos_q, pos_k, causal, scale)
     out["dq"] = rope(out["dq"][:, None, :], pos_q, theta, inverse=True)[:, 0, :]
     out["dk"] = rope(out["dk"][:, None, :], pos_k, theta, inverse=True)[:, 0, :]
     out["q_rot"], out["k_rot"] = qr, kr
     return out
+
+
+def attn_bwd_rope_heads(q, k, v, do, pos_q, pos_k, causal, scale, theta, heads=None):
+    """[B, S, H, D] layout over the selected heads, like `attn_bwd_heads`, for unrotated q and k."""
+    B, sq, H, D = q.shape
+    sk = k.shape[1]
+    heads = list(range(H)) if heads is None else list(heads)
+    nh = len(heads)
+    res = {"o": np.zeros((B, sq, nh, D)), "lse": np.zeros((B, sq, nh)), "delta": np.zeros((B, sq, nh)),
+           "dq": np.zeros((B, sq, nh, D)), "dk": np.zeros((B, sk, nh, D)), "dv": np.zeros((B, sk, nh, D))}
+    for b in range(B):
+        for n, h in enumerate(heads):
+            r = attn_bwd_rope(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], pos_q, pos_k, causal, scale, theta)
+            for key in res:
+                res[key][b, :, n] = r[key]
+    return res

@@ -192,3 +192,31 @@ def test_python_binding_rejects_bad_views():
         ea.ea_attn_fwd(q.float(), q, q, o, lse, [0, 8], [0, 8])
     with pytest.raises(ValueError):
         ea.ea_attn_fwd(q.transpose(1, 2), q, q, o, lse, [0, 8], [0, 8])
+
+
+def _rope(**kw):
+    a = dict(x=P, y=P + STEP, dt=1, B=1, H=32, S=1024, D=128, br=1024, seg=(0, 1024), theta=1e6, inv=0)
+    a.update(kw)
+    seg = (ctypes.c_int64 * len(a["seg"]))(*a["seg"])
+    vp = ctypes.c_void_p
+    return ea.lib().ea_rope(vp(a["x"]), vp(a["y"]), a["dt"], a["B"], a["H"], a["S"], a["D"], a["br"], seg,
+                            len(a["seg"]) // 2, a["theta"], a["inv"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), NULL), (dict(y=0), NULL),
+    (dict(B=0), SHAPE), (dict(H=0), SHAPE), (dict(S=-1), SHAPE), (dict(br=1000), SHAPE), (dict(S=1 << 31), SHAPE),
+    (dict(B=3, S=1 << 30, br=1 << 30, seg=(0, 1 << 30)), SHAPE),
+    (dict(D=96), UNSUP), (dict(dt=2), UNSUP), (dict(theta=0.0), UNSUP), (dict(theta=-1.0), UNSUP),
+    (dict(theta=float("inf")), UNSUP), (dict(theta=float("nan")), UNSUP), (dict(inv=2), UNSUP),
+    (dict(seg=(0, 1000)), POS), (dict(seg=(-1, 1024)), POS), (dict(seg=(0, 512, 0, 256, 0, 256)), POS),
+    (dict(seg=((1 << 31) - 10, 1024)), POS),
+    (dict(x=P + 8), ALIGN), (dict(y=P + STEP + 4), ALIGN),
+    (dict(y=P + 4096), ALIAS), (dict(x=P + STEP + 16 * 1024), ALIAS),
+])
+def test_rope_rejects_bad_arguments(kw, code):
+    assert _rope(**kw) == code
+
+
+def test_rope_empty_is_noop():
+    assert _rope(S=0, br=0, seg=(5, 0), x=0, y=0) == OK
