@@ -6,4 +6,4 @@ the merge rules: those live, independently, in ``oracle/`` and in the HIP
 library.
 """
 from .configs import CONFIGS, Config, get  # noqa: F401
-from .gen import normal_draw, rope_rotate_half, make_dense_case, make_ring_case  # noqa: F401
+from .gen import normal_draw, make_dense_case, make_ring_case  # noqa: F401

@@ -25,7 +25,7 @@ class Config:
     C: int = 0                # ring: chunk length (the sequence is 2*W chunks)
     rank: int = 0             # ring: which rank's share is computed
     std: float = 1.0          # standard deviation of the Gaussian draws
-    rope_theta: Optional[float] = None   # rotary base applied to Q and K before rounding
+    rope_theta: Optional[float] = None   # rotary base the attention step applies to Q and K (None: no rotation)
     seed: int = 0
 
     @property

@@ -1,12 +1,10 @@
-"""Seeded Gaussian draws rounded once to bf16, with optional rotary pre-rotation.
+"""Seeded Gaussian draws rounded once to bf16.
 
 Every tensor is drawn in fp32 from its own ``torch.Generator`` (seed =
 ``cfg.seed + 1000 * tensor_id + 10 * rank``; tensor ids Q=0, K=1, V=2, dO=3),
-scaled by ``cfg.std`` and, for Q and K of workloads with a rotary base, rotated
-in fp64 ("rotate-half" convention, angle = position * theta^(-2k/D)) before one
-round-to-nearest-even cast to bf16.  The rotary step only shapes the input
-distribution the way a Llama model with a raised base frequency would; the
-attention itself never sees positions through it.
+scaled by ``cfg.std`` and rounded once to bf16 (nearest even).  Q and K are the
+unrotated projections: a workload with a rotary base has its rotation applied by
+the code under test and, independently, by the oracle.
 
 Tensors are laid out [B, S, H, D] (D contiguous).  Draws happen on ``device``:
 CPU and GPU generators give different (each reproducible) streams, so a test
@@ -26,27 +24,6 @@ def normal_draw(shape, seed: int, std: float = 1.0, device="cpu") -> torch.Tenso
     return x
 
 
-def rope_rotate_half(x: torch.Tensor, theta: float, pos0: int = 0, head_chunk: int = 4) -> torch.Tensor:
-    """Rotate fp32 x [B, S, H, D] in place (fp64 arithmetic) for positions pos0..pos0+S-1."""
-    B, S, H, D = x.shape
-    half = D // 2
-    kk = torch.arange(half, dtype=torch.float64, device=x.device)
-    inv_freq = torch.pow(torch.tensor(theta, dtype=torch.float64, device=x.device), -2.0 * kk / D)
-    p = torch.arange(pos0, pos0 + S, dtype=torch.float64, device=x.device)
-    ang = p[:, None] * inv_freq[None, :]              # [S, half]
-    cos = torch.cos(ang)[None, :, None, :]
-    sin = torch.sin(ang)[None, :, None, :]
-    for h0 in range(0, H, head_chunk):
-        h1 = min(H, h0 + head_chunk)
-        xs = x[:, :, h0:h1, :].to(torch.float64)
-        a, b = xs[..., :half], xs[..., half:]
-        ra = a * cos - b * sin
-        rb = b * cos + a * sin
-        x[:, :, h0:h1, :half] = ra.to(torch.float32)
-        x[:, :, h0:h1, half:] = rb.to(torch.float32)
-    return x
-
-
 def _bf16(x: torch.Tensor) -> torch.Tensor:
     return x.to(torch.bfloat16)
 
@@ -61,8 +38,6 @@ def make_dense_case(cfg, device="cpu", with_grad_input=True, S=None, H=None):
         if name == "do" and not with_grad_input:
             continue
         x = normal_draw(shape, cfg.seed + 1000 * tid, cfg.std, device)
-        if cfg.rope_theta is not None and name in ("q", "k"):
-            rope_rotate_half(x, cfg.rope_theta)
         out[name] = _bf16(x)
         del x
     return out

@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the bench times.
 
 The whole workload (all heads, full sequence) runs on the GPU exactly as in
-bench.py.  The fp64 oracle then checks, per workload:
+bench.py, including the rotary embedding of Q and K (and the rotation of dQ and
+dK back) for the workloads with a rotary base.  The fp64 oracle then checks, per workload:
   * every output of a few whole heads where that finishes in seconds (C2), or
   * sampled query rows (O, LSE, dQ; each row's oracle cost is one pass over its
     keys) and sampled key rows whose attending queries are few (dK, dV), and
@@ -29,7 +30,7 @@ def _head_np(x, h):
 
 def _run_dense(cfg):
     t = synth.make_dense_case(cfg, DEV)
-    drv = ea.DenseCausal(t["q"], t["k"], t["v"], causal=True, scale=cfg.scale)
+    drv = ea.DenseCausal(t["q"], t["k"], t["v"], causal=True, scale=cfg.scale, rope_theta=cfg.rope_theta)
     drv.step(t["do"])
     torch.cuda.synchronize()
     return t, drv
@@ -42,36 +43,66 @@ def _sampled_rows(S, rng, n=24):
     return np.array(sorted(p for p in picks if 0 <= p < S))
 
 
-def _check_rows(name, t, drv, h, rows, pos_q, pos_k, scale):
+def _ref(q, k, v, do, pos_q, pos_k, scale, theta):
+    if theta is None:
+        return oracle.attn_bwd(q, k, v, do, pos_q, pos_k, True, scale)
+    return oracle.attn_bwd_rope(q, k, v, do, pos_q, pos_k, True, scale, theta)
+
+
+def _check_rows(name, t, drv, h, rows, pos_q, pos_k, scale, theta=None):
     q, k, v, do = (_head_np(t[n], h) for n in ("q", "k", "v", "do"))
-    ref = oracle.attn_bwd(q[rows], k, v, do[rows], pos_q[rows], pos_k, True, scale)
+    ref = _ref(q[rows], k, v, do[rows], pos_q[rows], pos_k, scale, theta)
     assert_close(f"{name} h{h} O(rows)", _head_np(drv.o, h)[rows], ref["o"])
     assert_lse(f"{name} h{h} LSE(rows)", _head_np(drv.lse, h)[rows], ref["lse"])
     assert_close(f"{name} h{h} dQ(rows)", _head_np(drv.dq, h)[rows], ref["dq"])
 
 
-def _check_tail_keys(name, t, drv, h, pos_q, pos_k, scale, n_keys=256):
+def _check_tail_keys(name, t, drv, h, pos_q, pos_k, scale, theta=None, n_keys=256):
     """The visible keys with the largest positions: all their queries fit in one oracle call."""
     visible = np.nonzero(pos_k <= pos_q.max())[0]
     keys = np.sort(visible[np.argsort(pos_k[visible])[-n_keys:]])
     kmin = pos_k[keys].min()
     qrows = np.nonzero(pos_q >= kmin)[0]
     q, k, v, do = (_head_np(t[n], h) for n in ("q", "k", "v", "do"))
-    ref = oracle.attn_bwd(q[qrows], k, v, do[qrows], pos_q[qrows], pos_k, True, scale)
+    ref = _ref(q[qrows], k, v, do[qrows], pos_q[qrows], pos_k, scale, theta)
     assert_close(f"{name} h{h} dK(tail keys)", _head_np(drv.dk, h)[keys], ref["dk"][keys])
     assert_close(f"{name} h{h} dV(tail keys)", _head_np(drv.dv, h)[keys], ref["dv"][keys])
 
 
-def _check_properties(name, t, drv, pos_q, pos_k):
+def _rotated_key_sums(dk, pos_k, theta, chunk=8192):
+    """sum_j R(pos_j) dK_j and sum_j |R(pos_j) dK_j| in fp64 (the gradient w.r.t. the rotated keys)."""
+    S, H, D = dk.shape
+    half = D // 2
+    f = torch.pow(torch.tensor(float(theta), dtype=torch.float64), -2.0 * torch.arange(half, dtype=torch.float64) / D)
+    f = f.to(DEV)
+    pk = torch.from_numpy(np.asarray(pos_k, dtype=np.int64)).to(DEV)
+    s = torch.zeros((H, D), dtype=torch.float64, device=DEV)
+    a = torch.zeros((H, D), dtype=torch.float64, device=DEV)
+    for j0 in range(0, S, chunk):
+        x = dk[j0:j0 + chunk].double()
+        ang = pk[j0:j0 + chunk, None].double() * f[None, :]
+        c, sn = torch.cos(ang)[:, None, :], torch.sin(ang)[:, None, :]
+        r = torch.cat([x[..., :half] * c - x[..., half:] * sn, x[..., half:] * c + x[..., :half] * sn], dim=-1)
+        s += r.sum(dim=0)
+        a += r.abs().sum(dim=0)
+    return s, a
+
+
+def _check_properties(name, t, drv, pos_q, pos_k, theta=None):
     # keys that no query may see
     dead = pos_k > pos_q.max()
     if dead.any():
         idx = torch.from_numpy(np.nonzero(dead)[0]).to(DEV)
         assert float(drv.dk[0, idx].abs().max()) == 0.0 and float(drv.dv[0, idx].abs().max()) == 0.0
-    # sum over keys of dK vanishes; sum over keys of dV equals the sum of dO (every row has keys here)
+    # sum over keys of dK vanishes (of the gradient w.r.t. the rotated keys, with a rotary base); sum over keys
+    # of dV equals the sum of dO (every row has keys here)
     f64 = torch.float64
-    sk = drv.dk[0].sum(dim=0, dtype=f64)                      # [H, D]
-    ak = drv.dk[0].abs().sum(dim=0, dtype=f64).clamp_min(1e-30)
+    if theta is None:
+        sk = drv.dk[0].sum(dim=0, dtype=f64)                      # [H, D]
+        ak = drv.dk[0].abs().sum(dim=0, dtype=f64).clamp_min(1e-30)
+    else:
+        sk, ak = _rotated_key_sums(drv.dk[0], pos_k, theta)
+        ak = ak.clamp_min(1e-30)
     sv = drv.dv[0].sum(dim=0, dtype=f64)
     sd = t["do"][0].sum(dim=0, dtype=f64)
     ratio = float((sk.abs() / ak).max())
@@ -89,14 +120,18 @@ def test_c2_full_heads():
     t, drv = _run_dense(cfg)
     pos = np.arange(cfg.S)
     heads = [0, cfg.H - 1, int(np.random.default_rng(cfg.seed).integers(1, cfg.H - 1))]
-    ref = oracle.attn_bwd_heads(t["q"], t["k"], t["v"], t["do"], pos, pos, True, cfg.scale, heads=heads)
+    if cfg.rope_theta is None:
+        ref = oracle.attn_bwd_heads(t["q"], t["k"], t["v"], t["do"], pos, pos, True, cfg.scale, heads=heads)
+    else:
+        ref = oracle.attn_bwd_rope_heads(t["q"], t["k"], t["v"], t["do"], pos, pos, True, cfg.scale,
+                                         cfg.rope_theta, heads=heads)
     got = {n: getattr(drv, n)[:, :, heads] for n in ("o", "lse", "dq", "dk", "dv")}
     assert_close("O", got["o"], ref["o"])
     assert_lse("LSE", got["lse"], ref["lse"])
     assert_close("dQ", got["dq"], ref["dq"])
     assert_close("dK", got["dk"], ref["dk"])
     assert_close("dV", got["dv"], ref["dv"])
-    _check_properties(cfg.name, t, drv, pos, pos)
+    _check_properties(cfg.name, t, drv, pos, pos, cfg.rope_theta)
 
 
 @pytest.mark.timeout(900)
@@ -108,9 +143,9 @@ def test_dense_sampled(key):
     pos = np.arange(cfg.S)
     rng = np.random.default_rng(cfg.seed)
     for h in (0, cfg.H - 1):
-        _check_rows(cfg.name, t, drv, h, _sampled_rows(cfg.S, rng), pos, pos, cfg.scale)
-        _check_tail_keys(cfg.name, t, drv, h, pos, pos, cfg.scale)
-    _check_properties(cfg.name, t, drv, pos, pos)
+        _check_rows(cfg.name, t, drv, h, _sampled_rows(cfg.S, rng), pos, pos, cfg.scale, cfg.rope_theta)
+        _check_tail_keys(cfg.name, t, drv, h, pos, pos, cfg.scale, cfg.rope_theta)
+    _check_properties(cfg.name, t, drv, pos, pos, cfg.rope_theta)
 
 
 @pytest.mark.timeout(900)
