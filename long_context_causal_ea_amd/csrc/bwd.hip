@@ -355,10 +355,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
       for (int u = 0; u < 16 / NKS; ++u) {
         const int r = (16 / NKS) * ks + u;
         const float pr = psrc[(r >> 2) * 256 + (r & 3)];
-        dsv[r] = pr * (dp_cur[r] - Ss[pstage][BQ + 8 * (r >> 2) + 4 * g + (r & 3)]);
+        const float ds = pr * (dp_cur[r] - Ss[pstage][BQ + 8 * (r >> 2) + 4 * g + (r & 3)]);
+        dsv[r] = prev ? ds : 0.f;  // step 0 has no tile t-1: add zeros (keeps the accumulation unconditional)
       }
     }
-    if (prev) accumulate(RB{}, pstage, dsv);
+    // at step 0 the zeros multiply tile 0's Q (resident, finite) rather than a stage never loaded
+    accumulate(RB{}, prev ? pstage : stage, dsv);
   };
 
   // Wave 0, which loads the per-row statistics, rewrites the LSE of a resident
@@ -380,40 +382,50 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     // Step t reads tiles t-1, t, t+1 and loads tile t+NST-2 into the stage of
-    // tile t-2.  Unrolled by two so that the two score buffers alternate.
-    f32x16 sa, sb;  // role A: scores; role B: dP
-    int ca = kFull, cb = kFull;
-    if (role == 0) {
-      ca = classify(0);
-      scores(RA{}, 0, sa);
-    }
-    int st = 0;  // stage of tile t
-    auto body = [&](int t, f32x16& x_cur, int& c_cur, f32x16& x_nx, int& c_nx) {
-      if (t > 0) wait_ring(std::integral_constant<int, AHEAD>{});  // tile t+1 resident; all past step t-1
-      const int sp = st == 0 ? NST - 1 : st - 1;
-      const int sf = st >= 2 ? st - 2 : st + NST - 2;
-      issue_tile(sf, t + NST - 2);
-      to_log2(st + 1 == NST ? 0 : st + 1);  // tile t+1, read from step t+1 on
-      if (role == 0)
-        step_a(st, t, x_cur, c_cur, x_nx, c_nx);
-      else
-        step_b(st, sp, std::true_type{}, t, x_cur, x_nx);
-      st = st + 1 == NST ? 0 : st + 1;
+    // tile t-2.  Unrolled by two so that the two score buffers alternate.  Each
+    // role runs its own copy of the loop (the role is uniform per wave), so that
+    // its accumulators keep their registers from one iteration to the next.
+    auto run = [&](auto ROLE) {
+      constexpr int R = decltype(ROLE)::value;
+      f32x16 sa, sb;  // role A: scores; role B: dP
+      int ca = kFull, cb = kFull;
+      if constexpr (R == 0) {
+        ca = classify(0);
+        scores(RA{}, 0, sa);
+      }
+      int st = 0;  // stage of tile t
+      auto body = [&](int t, f32x16& x_cur, int& c_cur, f32x16& x_nx, int& c_nx) {
+        if (t > 0) wait_ring(std::integral_constant<int, AHEAD>{});  // tile t+1 resident; all past step t-1
+        const int sp = st == 0 ? NST - 1 : st - 1;
+        const int sf = st >= 2 ? st - 2 : st + NST - 2;
+        issue_tile(sf, t + NST - 2);
+        if constexpr (R == 0) {
+          to_log2(st + 1 == NST ? 0 : st + 1);  // tile t+1, read from step t+1 on
+          step_a(st, t, x_cur, c_cur, x_nx, c_nx);
+        } else {
+          step_b(st, sp, std::true_type{}, t, x_cur, x_nx);
+        }
+        st = st + 1 == NST ? 0 : st + 1;
+      };
+      for (int t = 0; t < nt; t += 2) {
+        body(t, sa, ca, sb, cb);
+        if (t + 1 >= nt) break;
+        body(t + 1, sb, cb, sa, ca);
+      }
+      // role B's last step: dS and dK of tile nt-1 (P(nt-1) published in step nt-1)
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if constexpr (R == 1) {
+        f32x16 last = (nt % 2 == 1) ? sb : sa;  // dP(nt-1): into sb for even nt-1, sa for odd
+        f32x16 dummy;
+        const int sp = st == 0 ? NST - 1 : st - 1;  // st is now the stage of tile nt
+        step_b(st, sp, std::false_type{}, nt, last, dummy);
+      }
     };
-    for (int t = 0; t < nt; t += 2) {
-      body(t, sa, ca, sb, cb);
-      if (t + 1 >= nt) break;
-      body(t + 1, sb, cb, sa, ca);
-    }
-    // role B's last step: dS and dK of tile nt-1 (P(nt-1) published in step nt-1)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (role == 1) {
-      f32x16 last = (nt % 2 == 1) ? sb : sa;  // dP(nt-1): into sb for even nt-1, sa for odd
-      f32x16 dummy;
-      const int sp = st == 0 ? NST - 1 : st - 1;  // st is now the stage of tile nt
-      step_b(st, sp, std::false_type{}, nt, last, dummy);
-    }
+    if (role == 0)
+      run(RA{});
+    else
+      run(RB{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // retire the trailing (unused) loads
   }
 
