@@ -422,10 +422,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
         step_b(st, sp, std::false_type{}, nt, last, dummy);
       }
     };
-    if (role == 0)
+    if (role == 0) {
       run(RA{});
-    else
+    } else {
+      // issue priority for the V-side waves: their dP products open each step
+      // while the K-side waves of the same SIMD are still in the exponentials
+      __builtin_amdgcn_s_setprio(1);
       run(RB{});
+      __builtin_amdgcn_s_setprio(0);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // retire the trailing (unused) loads
   }
 
