@@ -88,6 +88,9 @@ CASES = [
     (128, 1, 450, 1, True, [0, 450], [0, 1], torch.float32),
     (128, 1, 190, 190, True, [0, 190], [100, 190], torch.float32),  # rows 0..99 see no key
     (64, 3, 70, 130, False, [0, 70], [0, 130], torch.bfloat16),
+    # positions at the top of the range (every position < 2^31)
+    (128, 1, 300, 400, True, [2 ** 31 - 300, 300], [2 ** 31 - 500, 400], torch.float32),
+    (64, 1, 200, 200, True, [2 ** 31 - 200, 100, 1000, 100], [2 ** 31 - 150, 150, 0, 50], torch.float32),
 ]
 
 
@@ -212,3 +215,13 @@ def test_zigzag_ring_small(rank, C, D):
     assert_close("dQ", drv.dq, ref["dq"])
     assert_close("dK", drv.dk, ref["dk"])
     assert_close("dV", drv.dv, ref["dv"])
+
+
+def test_bitwise_reproducible():
+    """No atomics anywhere: two runs of the same call give identical bits (O, LSE, dQ, dK, dV)."""
+    banner("bitwise reproducibility, D=128 S=700 causal")
+    q, k, v, do = (_rand((1, 700, 4, 128), 90 + i) for i in range(4))
+    a = _run_dense(q, k, v, do, [0, 700], [0, 700], True)
+    b = _run_dense(q, k, v, do, [0, 700], [0, 700], True)
+    for name in ("o", "lse", "dq", "dk", "dv", "delta"):
+        assert torch.equal(a[name], b[name]), name
