@@ -106,10 +106,14 @@ __device__ __forceinline__ float lse_to_log2(float l) {
 // row-major tiles by the LDS transpose read.
 //
 // 32-row query tiles (Q, dO, LSE, Delta) stream through a 6-stage LDS ring of
-// direct global->LDS loads (tiles t-1 .. t+1 in use, t+2 .. t+4 in flight).  In step t, A computes the scores of tile t+1 while
-// turning those of tile t into P (software pipeline) and publishes P(t); B
-// computes dP(t) while forming dS(t-1) from P(t-1), published one step earlier,
-// so the one workgroup barrier per step orders both the ring and the exchange.
+// direct global->LDS loads (tiles t-1 .. t+1 in use, t+2 .. t+4 in flight).  In
+// step t, A computes the scores of tile t+1 while turning those of tile t into
+// P (software pipeline) and publishes P(t); B computes dP(t) while forming
+// dS(t-1) from P(t-1), published one step earlier, so the one workgroup barrier
+// per step orders both the ring and the exchange.  Each role runs its own copy
+// of the loop so that its accumulator stays in the same registers, and B runs at
+// issue priority 1 (its dP products open every step while A is still in the
+// exponentials).
 template <int D>
 struct DkdvCfg {
   static constexpr int NW = 8, NT = 512, BKV = 128, BQ = 32, NST = 6;
