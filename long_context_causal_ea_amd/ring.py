@@ -20,10 +20,42 @@ gradients are with respect to the unrotated inputs.
 
 All buffers are allocated when the driver is built; ``forward`` and
 ``backward`` enqueue work on the current stream and allocate nothing.
+
+``zigzag_shard`` / ``zigzag_unshard`` move a whole sequence to and from the
+ranks' local orders (the input preparation that hands each rank its share with
+its positions, cn486.com page, usage code); they are plain tensor copies along
+the sequence axis, laid out by ``ea_zigzag_segments``.
 """
 import torch
 
 from . import _lib as L
+
+
+def zigzag_shard(x, world: int, rank: int, dim: int = 1):
+    """The rows of x (whole sequence along `dim`) that rank `rank` of a `world`-rank zigzag ring holds, in its
+    local order (a copy)."""
+    s_total = x.shape[dim]
+    seg = L.ea_zigzag_segments(s_total, world, rank)
+    parts = [x.narrow(dim, seg[i], seg[i + 1]) for i in range(0, len(seg), 2) if seg[i + 1] > 0]
+    return torch.cat(parts, dim=dim)
+
+
+def zigzag_unshard(parts, world: int, dim: int = 1):
+    """Inverse of `zigzag_shard`: the whole sequence from the `world` ranks' local tensors (rank order)."""
+    if len(parts) != world:
+        raise ValueError("one local tensor per rank")
+    local = parts[0].shape[dim]
+    s_total = local * world
+    shape = list(parts[0].shape)
+    shape[dim] = s_total
+    out = parts[0].new_empty(shape)
+    for r, x in enumerate(parts):
+        seg = L.ea_zigzag_segments(s_total, world, r)
+        off = 0
+        for i in range(0, len(seg), 2):
+            out.narrow(dim, seg[i], seg[i + 1]).copy_(x.narrow(dim, off, seg[i + 1]))
+            off += seg[i + 1]
+    return out
 
 
 class DenseCausal:
