@@ -66,7 +66,10 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
   using IO = RopeIO<BF16>;
   constexpr int HALF = D / 2, EPC = IO::EPC, CPH = HALF / EPC;  // chunks per half row
   constexpr int ESZ = BF16 ? 2 : 4;
-  __shared__ float2 cs[kRopeRows][HALF];
+  // (cos, sin) of angle k at slot k + k / EPC: the chunks a wave reads together
+  // (one per lane group) then fall on distinct LDS banks
+  constexpr int SLOTS = HALF + HALF / EPC;
+  __shared__ float2 cs[kRopeRows][SLOTS];
 
   const int tid = threadIdx.x;
   const int row0 = blockIdx.x * kRopeRows;
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
     red = __builtin_fma(-n, kTwoPiLo, red);
     double s, c;
     sincos(red, &s, &c);
-    cs[r][k] = make_float2((float)c, (float)(p.inverse ? -s : s));
+    cs[r][k + k / EPC] = make_float2((float)c, (float)(p.inverse ? -s : s));
   }
   __syncthreads();
 
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
     float ylo[EPC], yhi[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
-      const float2 t = cs[r][c * EPC + e];
+      const float2 t = cs[r][c * (EPC + 1) + e];
       ylo[e] = __builtin_fmaf(lo[e], t.x, -hi[e] * t.y);
       yhi[e] = __builtin_fmaf(hi[e], t.x, lo[e] * t.y);
     }
