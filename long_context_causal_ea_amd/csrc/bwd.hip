@@ -13,7 +13,7 @@
 //             the B-operand form that dV^T += dO^T P and dK^T += Q^T dS need;
 //             the dO^T and Q^T operands are read from the row-major tiles with
 //             the LDS transpose read.
-//  3. dq:     one workgroup per 128-query block, streaming key/value tiles
+//  3. dq:     one workgroup (8 waves, two per SIMD) per 256-query block, streaming key/value tiles
 //             through a direct-to-LDS ring like the forward; recomputes S^T and
 //             dP^T with the query on the lane axis and accumulates
 //             dQ^T += K^T dS^T in registers (K^T by transpose read of the
@@ -454,7 +454,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------ dQ
-// One workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
+// One workgroup = 8 waves = 256 query rows of one (batch, head), two waves per
+// SIMD, so each key/value tile in LDS serves eight waves; each wave owns
 // 32 rows and keeps their Q and dO rows as MFMA B operands and its dQ^T
 // accumulator in registers.  Key/value tiles of 32 rows stream through a
 // 4-stage direct-to-LDS ring (K and V of a stage side by side), three tiles in
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 // of tile t.
 template <int D>
 struct DqCfg {
-  static constexpr int NW = 4, BQ = 32 * NW, BK = 32, NT = 64 * NW, NST = 4;
+  static constexpr int NW = 8, BQ = 32 * NW, BK = 32, NT = 64 * NW, NST = 4;
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;             // rows one direct-to-LDS load covers
   static constexpr int NLT = BK / RPI;             // loads per tile (each of K and V)
@@ -475,7 +476,7 @@ struct DqCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p) {
   using Cfg = DqCfg<D>;
   constexpr int BQ = Cfg::BQ, BK = Cfg::BK, CPR = Cfg::CPR, NST = Cfg::NST, RPI = Cfg::RPI;
   constexpr int NKS = D / 16, NDB = D / 32, KT = Cfg::LDS_T;
@@ -763,7 +764,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   p.nblk = (a.Sq + DqCfg<128>::BQ - 1) / DqCfg<128>::BQ;
   const long nwg = (long)a.B * a.H * p.nblk;
   if (nwg == 0 || a.Sk == 0) return hipSuccess;
-  dim3 grid((unsigned)nwg), block(256);
+  dim3 grid((unsigned)nwg), block(DqCfg<128>::NT);
   if (a.D == 64)
     hipLaunchKernelGGL(dq_kernel<64>, grid, block, 0, stream, p);
   else
