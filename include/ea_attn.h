@@ -1,6 +1,8 @@
 /*
  * ea_attn: blockwise causal attention (forward, backward, LSE merge) for one
- * sequence-parallel rank's share of a long sequence, on AMD MI355X (gfx950).
+ * sequence-parallel rank's share of a long sequence, on AMD MI355X (gfx950),
+ * with the rotary position embedding and the fused cross-entropy of the same
+ * training step (ea_rope, ea_xent_fwd_bwd, declared further below).
  *
  * The operations follow the EasyContext pages:
  *  - ring attention cuts one sequence over GPUs; each rank attends its local
@@ -67,7 +69,7 @@ enum ea_status {
   EA_OK = 0,
   EA_ERR_NULL = 1,         /* a required pointer is NULL */
   EA_ERR_SHAPE = 2,        /* B, H, S, batch_rows out of range */
-  EA_ERR_UNSUPPORTED = 3,  /* D, dtype, mask mode or scale not supported */
+  EA_ERR_UNSUPPORTED = 3,  /* D, dtype, mask mode, scale or another parameter not supported */
   EA_ERR_POSITIONS = 4,    /* bad segment count, lengths, starts or positions >= 2^31 */
   EA_ERR_ALIGN = 5,        /* pointer misaligned */
   EA_ERR_ALIAS = 6,        /* an output overlaps an input */

@@ -128,7 +128,7 @@ const char* ea_strerror(int status) {
     case EA_OK: return "ok";
     case EA_ERR_NULL: return "a required pointer is NULL";
     case EA_ERR_SHAPE: return "B, H, sequence length or batch row stride out of range";
-    case EA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype, mask mode or scale";
+    case EA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype, mask mode, scale or other parameter";
     case EA_ERR_POSITIONS: return "bad position segments (count, lengths, starts, or a position >= 2^31)";
     case EA_ERR_ALIGN: return "pointer misaligned (the alignment each call documents in ea_attn.h)";
     case EA_ERR_ALIAS: return "an output buffer overlaps an input buffer";
