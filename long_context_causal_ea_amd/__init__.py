@@ -11,4 +11,6 @@ from ._lib import (  # noqa: F401
     ea_kernel_name, ea_lse_merge, ea_profile_begin, ea_profile_end, ea_profile_query, ea_ring_source, ea_rope,
     ea_version, ea_xent_fwd_bwd, ea_zigzag_segments, lib, strerror,
 )
-from .ring import DenseCausal, ZigzagRingRank, zigzag_shard, zigzag_unshard  # noqa: F401
+from .ring import (  # noqa: F401
+    DenseCausal, ZigzagRingRank, ulysses_shard, ulysses_unshard, zigzag_shard, zigzag_unshard,
+)

@@ -21,6 +21,11 @@ gradients are with respect to the unrotated inputs.
 All buffers are allocated when the driver is built; ``forward`` and
 ``backward`` enqueue work on the current stream and allocate nothing.
 
+``ulysses_shard`` / ``ulysses_unshard`` do the same for the head split of the
+Ulysses mode (mlqm.cn walkthrough, parallel modes): after its all-to-all a rank
+holds every token of H / world heads, and its attention is one ``DenseCausal``
+over them.
+
 ``zigzag_shard`` / ``zigzag_unshard`` move a whole sequence to and from the
 ranks' local orders (the input preparation that hands each rank its share with
 its positions, cn486.com page, usage code); they are plain tensor copies along
@@ -38,6 +43,21 @@ def zigzag_shard(x, world: int, rank: int, dim: int = 1):
     seg = L.ea_zigzag_segments(s_total, world, rank)
     parts = [x.narrow(dim, seg[i], seg[i + 1]) for i in range(0, len(seg), 2) if seg[i + 1] > 0]
     return torch.cat(parts, dim=dim)
+
+
+def ulysses_shard(x, world: int, rank: int, dim: int = 2):
+    """The heads of x ([B, S, H, D], whole sequence) that rank `rank` of a `world`-way Ulysses split holds after
+    the sequence-to-head all-to-all: heads [rank * H / world, (rank + 1) * H / world), every token (a copy)."""
+    H = x.shape[dim]
+    if H % world:
+        raise ValueError("the head count must be a multiple of the world size")
+    hw = H // world
+    return x.narrow(dim, rank * hw, hw).contiguous()
+
+
+def ulysses_unshard(parts, dim: int = 2):
+    """Inverse of `ulysses_shard` (the head-to-sequence all-to-all gathered on one device)."""
+    return torch.cat(list(parts), dim=dim)
 
 
 def zigzag_unshard(parts, world: int, dim: int = 1):

@@ -70,6 +70,9 @@ CONFIGS = {
                  S=131072, std=0.5, rope_theta=1e9, seed=1005),
     "t": Config("causal-b1-h32-d128-s65536-rope1e6", "dense", B=1, H=32, D=128, S=65536,
                 rope_theta=1e6, seed=1006),
+    # one GPU's share of an 8-way Ulysses split of the 512K-token Llama-2-7B attention: after the
+    # sequence-to-head all-to-all a GPU holds every token of 32 / 8 = 4 heads
+    "u3": Config("ulysses-512k-w8-h4-d128", "dense", B=1, H=4, D=128, S=524288, seed=1007),
 }
 
 

@@ -135,7 +135,7 @@ def test_c2_full_heads():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("key", ["t", "c5"])
+@pytest.mark.parametrize("key", ["t", "c5", "u3"])
 def test_dense_sampled(key):
     cfg = synth.get(key)
     banner(cfg.name)

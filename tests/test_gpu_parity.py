@@ -267,3 +267,27 @@ def test_zigzag_ring_all_ranks_reassemble(W, C, theta):
         # and the two paths of the library agree with each other within the same bars
         assert_close(f"{n} (ring) vs dense", got[n], getattr(dense, n))
     assert_lse("LSE (ring)", got["lse"], ref["lse"])
+
+
+def test_ulysses_ranks_match_the_whole_layer():
+    """Every rank of a 4-way Ulysses split (H / 4 heads over all tokens each), run on this GPU and gathered
+    over heads: bit-identical to the dense driver over all heads (each head's arithmetic does not depend on the
+    others), and within the bars of the oracle."""
+    W, S, H, D = 4, 300, 8, 128
+    banner(f"ulysses W={W} S={S} H={H}")
+    q, k, v, do = (_rand((1, S, H, D), 500 + i) for i in range(4))
+    outs = {n: [] for n in ("o", "lse", "dq", "dk", "dv")}
+    for r in range(W):
+        drv = ea.DenseCausal(*(ea.ulysses_shard(x, W, r) for x in (q, k, v)), causal=True)
+        drv.step(ea.ulysses_shard(do, W, r))
+        for n in outs:
+            outs[n].append(getattr(drv, n).clone())
+    whole = ea.DenseCausal(q, k, v, causal=True)
+    whole.step(do)
+    torch.cuda.synchronize()
+    for n, parts in outs.items():
+        assert torch.equal(ea.ulysses_unshard(parts), getattr(whole, n)), n
+    pos = np.arange(S)
+    ref = oracle.attn_bwd_heads(q, k, v, do, pos, pos, True, scale_of(D))
+    for n in ("o", "dq", "dk", "dv"):
+        assert_close(n, ea.ulysses_unshard(outs[n]), ref[n])

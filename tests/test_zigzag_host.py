@@ -32,3 +32,13 @@ def test_unshard_inverts_shard(W, C):
 def test_unshard_needs_every_rank():
     with pytest.raises(ValueError):
         ea.zigzag_unshard([torch.zeros(1, 4, 1, 1)], 2)
+
+
+def test_ulysses_shard_round_trip():
+    x = torch.randn(2, 10, 8, 4)
+    parts = [ea.ulysses_shard(x, 4, r) for r in range(4)]
+    assert all(p.shape == (2, 10, 2, 4) and p.is_contiguous() for p in parts)
+    assert torch.equal(parts[3], x[:, :, 6:8])
+    assert torch.equal(ea.ulysses_unshard(parts), x)
+    with pytest.raises(ValueError):
+        ea.ulysses_shard(x, 3, 0)
