@@ -142,7 +142,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   const int role = w >> 2, kw = w & 3;
   const int ln = lane & 31, g = lane >> 5;
 
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int work = xcd_remap(blockIdx.x, gridDim.x, p.nblk);
   const int bh = work / p.nblk;
   const int kb = work % p.nblk;  // lowest keys first: under the causal rule they see the most queries
   const int b = bh / p.H, h = bh % p.H;
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
   const int ln = lane & 31, g = lane >> 5;
 
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int work = xcd_remap(blockIdx.x, gridDim.x, p.nblk);
   const int bh = work / p.nblk;
   const int qb = p.nblk - 1 - work % p.nblk;  // longest query blocks first
   const int b = bh / p.H, h = bh % p.H;

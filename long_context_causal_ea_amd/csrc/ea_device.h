@@ -217,14 +217,31 @@ __device__ __forceinline__ bool in_window(const QueryWindow& w, int i) {
 
 enum TileClass { kSkip = 0, kFull = 1, kPartial = 2 };
 
-// Hardware places workgroup `bid` on XCD bid % 8.  Give each XCD a contiguous
-// slice of the work list so that neighbouring work items (same batch and head,
-// hence the same keys/values) share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
-  int xcd = bid % kNumXcd, slot = bid / kNumXcd;
-  int per = nwg / kNumXcd, rem = nwg % kNumXcd;
-  int start = xcd * per + (xcd < rem ? xcd : rem);
-  return start + slot;
+// Hardware places workgroup `bid` on XCD bid % 8 and each XCD runs its share in
+// dispatch order, so the work an XCD receives is fixed at launch.  The work list
+// is (batch*head) major with `per_bh` items per head, longest first within a
+// head.  When every XCD's contiguous slice of the list holds whole heads, the
+// slices carry equal work and one head's tiles stay in one XCD's L2: use them.
+// Otherwise (say 4 heads over 8 XCDs, where contiguous slices would give half the
+// XCDs the long end of a causal triangle and 1.5x the mean work) deal the list in
+// rounds of kXcdChunk consecutive items per XCD, the order of the XCDs reversed on
+// every other round: neighbouring items still run side by side on one XCD, and
+// the alternation evens out the items' decreasing sizes.  Both are bijections on
+// [0, nwg).
+constexpr int kXcdChunk = 32;  // workgroups resident on one XCD (32 CUs, one each)
+
+__device__ __forceinline__ int xcd_remap(int bid, int nwg, int per_bh) {
+  const int x = bid % kNumXcd, s = bid / kNumXcd;
+  const int per = nwg / kNumXcd, rem = nwg % kNumXcd;
+  if (nwg % (kNumXcd * per_bh) == 0) return x * per + s;
+  const int rfull = per / kXcdChunk, r = s / kXcdChunk;
+  if (r < rfull) {
+    const int chunk = (r & 1) ? (kNumXcd - 1 - x) : x;
+    return (r * kNumXcd + chunk) * kXcdChunk + s % kXcdChunk;
+  }
+  // last, partial round: contiguous slices of what is left
+  const int per2 = per - rfull * kXcdChunk;
+  return rfull * kNumXcd * kXcdChunk + x * per2 + (x < rem ? x : rem) + (s - rfull * kXcdChunk);
 }
 
 }  // namespace ea

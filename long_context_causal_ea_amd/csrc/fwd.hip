@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   const int ln = lane & 31, g = lane >> 5;
 
   // ---- work item: (batch*head) major, longest query blocks first
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int work = xcd_remap(blockIdx.x, gridDim.x, p.nqb);
   const int bh = work / p.nqb;
   const int qb = p.nqb - 1 - work % p.nqb;
   const int b = bh / p.H, h = bh % p.H;

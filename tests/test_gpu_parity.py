@@ -269,6 +269,26 @@ def test_zigzag_ring_all_ranks_reassemble(W, C, theta):
     assert_lse("LSE (ring)", got["lse"], ref["lse"])
 
 
+def test_work_mapping_covers_every_item():
+    """Five heads of 16484 tokens: the work lists (65 query blocks, 129 key blocks per head) do not split into
+    whole heads per XCD, so the launches deal them out in rounds with a ragged last round.  Each head's results
+    must be bit-identical to a launch over that head alone, whose list is dealt in contiguous slices: every work
+    item is computed exactly once under both mappings."""
+    B, S, H, D = 1, 16484, 5, 128
+    banner(f"work mapping S={S} H={H}")
+    q, k, v, do = (_rand((B, S, H, D), 700 + i) for i in range(4))
+    whole = ea.DenseCausal(q, k, v, causal=True)
+    whole.step(do)
+    torch.cuda.synchronize()
+    for h in range(H):
+        one = ea.DenseCausal(*(x[:, :, h:h + 1].contiguous() for x in (q, k, v)), causal=True)
+        one.step(do[:, :, h:h + 1].contiguous())
+        torch.cuda.synchronize()
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            a, b = getattr(whole, n), getattr(one, n)
+            assert torch.equal(a[:, :, h:h + 1], b), (h, n)
+
+
 def test_ulysses_ranks_match_the_whole_layer():
     """Every rank of a 4-way Ulysses split (H / 4 heads over all tokens each), run on this GPU and gathered
     over heads: bit-identical to the dense driver over all heads (each head's arithmetic does not depend on the
