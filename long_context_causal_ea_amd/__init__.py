@@ -12,5 +12,5 @@ from ._lib import (  # noqa: F401
     ea_version, ea_xent_fwd_bwd, ea_zigzag_segments, lib, strerror,
 )
 from .ring import (  # noqa: F401
-    DenseCausal, ZigzagRingRank, ulysses_shard, ulysses_unshard, zigzag_shard, zigzag_unshard,
+    DenseCausal, ZigzagRingRank, capture_step, ulysses_shard, ulysses_unshard, zigzag_shard, zigzag_unshard,
 )

@@ -19,7 +19,9 @@ owns) and the backward rotates dQ and dK back (the transpose, in place), so the
 gradients are with respect to the unrotated inputs.
 
 All buffers are allocated when the driver is built; ``forward`` and
-``backward`` enqueue work on the current stream and allocate nothing.
+``backward`` enqueue work on the given stream (default: the current one) and
+allocate nothing, so a whole step can be recorded as a HIP graph
+(``capture_step``), alone or inside a caller's larger captured training step.
 
 ``ulysses_shard`` / ``ulysses_unshard`` do the same for the head split of the
 Ulysses mode (mlqm.cn walkthrough, parallel modes): after its all-to-all a rank
@@ -78,6 +80,31 @@ def zigzag_unshard(parts, world: int, dim: int = 1):
     return out
 
 
+def _zero(stream, *ts):
+    """Zero fp32 accumulators on the stream the library calls use (torch's fill kernel, no memset)."""
+    if stream is None:
+        for t in ts:
+            t.zero_()
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    with torch.cuda.stream(s):
+        for t in ts:
+            t.zero_()
+
+
+def capture_step(driver, do):
+    """Record one whole ``driver.step(do)`` (rotations, forward, merges, zeroing, backward) as a HIP graph.
+
+    Returns a ``torch.cuda.CUDAGraph``; ``replay()`` reruns every launch of the step on the current stream.  The
+    graph holds the driver's buffers and ``do`` by address: to run on new inputs, copy them into the same tensors
+    (the driver's inputs and ``do``) before replaying.  Nothing in the step allocates or clears memory with a
+    memset, so the recorded step is the eager one launch for launch."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        driver.step(do)
+    return g
+
+
 class DenseCausal:
     def __init__(self, q, k, v, causal=True, scale=None, o_dtype=torch.float32, rope_theta=None):
         B, S, H, D = q.shape
@@ -108,9 +135,7 @@ class DenseCausal:
                       stream)
 
     def backward(self, do, stream=None):
-        self.dq.zero_()
-        self.dk.zero_()
-        self.dv.zero_()
+        _zero(stream, self.dq, self.dk, self.dv)
         L.ea_attn_bwd(self.q, self.k, self.v, self.o, do, self.lse, self.delta, self.dq, self.dk, self.dv,
                       self.q_seg, self.k_seg, self.causal, self.scale, delta_ready=False, stream=stream)
         if self.rope_theta is not None:
@@ -187,9 +212,7 @@ class ZigzagRingRank:
                 L.ea_lse_merge(self.o, self.lse, self.o_part, self.lse_part, stream)
 
     def backward(self, do, stream=None):
-        self.dq.zero_()
-        self.dk.zero_()
-        self.dv.zero_()
+        _zero(stream, self.dq, self.dk, self.dv)
         for t in range(self.W):
             kb, vb = self._block(t, self.k), self._block(t, self.v)
             L.ea_attn_bwd(self.q, kb, vb, self.o, do, self.lse, self.delta, self.dq, self._block(t, self.dk),
