@@ -9,8 +9,9 @@
 //    tiles of 64 rows (two 32-key blocks) stream through a ring of LDS stages
 //    filled by direct global->LDS loads, three tiles in flight, so one barrier
 //    covers 32 matrix-core products per wave.
-//  - The loop is software-pipelined: the scores of tile t+1 are issued to the
-//    matrix cores while the softmax of tile t runs on the vector ALUs.
+//  - The loop is software-pipelined: each step first issues the scores of tile
+//    t+1 to the matrix cores, then runs the softmax of tile t (row maximum,
+//    rescale, exponentials) on the vector ALUs while they execute.
 //  - Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
 //    every lane then holds 32 scores of ONE query row, so the row max and row
 //    sum are in-lane reductions plus one exchange with lane l^32.
@@ -221,8 +222,8 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
 
   using I0 = std::integral_constant<int, 0>;
 
-  // one pipeline step: softmax and P V of tile t (scores in st_cur, stage STAGE)
-  // interleaved with the scores of tile t+1 (into st_next, stage STAGE+1)
+  // one pipeline step: the scores of tile t+1 (into st_next, stage STAGE+1), then
+  // the softmax and P V of tile t (scores in st_cur, stage STAGE)
   auto step = [&](auto STAGE, int t, f32x16 (&st_cur)[NMB], int& cls_cur, f32x16 (&st_next)[NMB], int& cls_next) {
     constexpr int stage = decltype(STAGE)::value;
     constexpr int nstage = (stage + 1) % NST, fstage = (stage + NST - 1) % NST;
@@ -242,6 +243,11 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
           st_cur[mb][r] = in_window(kwin, j) ? st_cur[mb][r] : NEG_INF;
         }
     }
+    // The scores of tile t+1 go to the matrix cores first: they do not depend on
+    // the softmax of tile t, so its maximum, rescale and exponentials (vector
+    // ALUs) run while they execute.  On the last tile the scores of a dummy tile
+    // are computed and dropped.
+    scores(std::integral_constant<int, nstage>{}, st_next);
     float mx = NEG_INF;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -257,10 +263,6 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
       m_run = mnew;
     }
 
-    // One straight-line block: the scores of tile t+1 (matrix cores) do not
-    // depend on the softmax of tile t (vector ALUs), so the two interleave.  On
-    // the last tile the scores of a dummy tile are computed and dropped.
-    scores(std::integral_constant<int, nstage>{}, st_next);
     const float msub = (m_run == NEG_INF) ? 0.f : m_run * p.c;
     bf16x8 pb[2 * NMB];  // P^T as B operands, one per 16-key k-step
 #pragma unroll
