@@ -95,6 +95,26 @@ int ea_attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtyp
                 int mask_mode, float scale, void* stream);
 
 /*
+ * Forward merged into an accumulator: the partial result of this call (O_part,
+ * LSE_part as ea_attn_fwd defines them) is combined into the fp32 accumulator
+ * (o_acc, lse_acc) exactly as ea_lse_merge combines a stored partial, in the
+ * same launch, so a ring step's partial never goes through memory (the ring
+ * combines one partial per visited share: hotelren.com page, section 1).
+ * o_acc [B,Sq,H,D] and lse_acc [B,Sq,H] are fp32, read and written in place
+ * (same layout and row stride q_batch_rows as q); every other argument is as
+ * for ea_attn_fwd.  A row with no allowed key in this call leaves its
+ * accumulator unchanged (both -inf gives (0, -inf)), so Sk == 0 changes
+ * nothing but such rows.  o_acc and lse_acc must not overlap q, k, v or each
+ * other.  Results equal ea_attn_fwd into a separate fp32 partial followed by
+ * ea_lse_merge, up to the order of rounding.
+ */
+int ea_attn_fwd_merge(const void* q, const void* k, const void* v, float* o_acc, float* lse_acc,
+                      int B, int H, int64_t Sq, int64_t Sk, int D,
+                      int64_t q_batch_rows, int64_t k_batch_rows,
+                      const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg,
+                      int mask_mode, float scale, void* stream);
+
+/*
  * Backward by recomputation from the saved statistics (the recompute-and-tile
  * gradient of the hotelren.com page, section 2).  With P_ij =
  * exp(scale*<q_i,k_j> - LSE_i) on allowed pairs (0 elsewhere):

@@ -42,6 +42,9 @@ def lib():
     L.ea_attn_fwd.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i64, i64, i32, i64, i64,
                               pi64, i32, pi64, i32, i32, f32, vp]
     L.ea_attn_fwd.restype = i32
+    L.ea_attn_fwd_merge.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i32, i64, i64,
+                                    pi64, i32, pi64, i32, i32, f32, vp]
+    L.ea_attn_fwd_merge.restype = i32
     L.ea_attn_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, i32, i32, i64, i64, i32,
                               i64, i64, pi64, i32, pi64, i32, i32, f32, vp]
     L.ea_attn_bwd.restype = i32
@@ -73,7 +76,7 @@ def lib():
     return L
 
 
-EXPORTS = ("ea_attn_fwd", "ea_attn_bwd", "ea_lse_merge", "ea_xent_fwd_bwd", "ea_rope", "ea_zigzag_segments",
+EXPORTS = ("ea_attn_fwd", "ea_attn_fwd_merge", "ea_attn_bwd", "ea_lse_merge", "ea_xent_fwd_bwd", "ea_rope", "ea_zigzag_segments",
            "ea_ring_source",
            "ea_strerror", "ea_last_hip_error", "ea_version", "ea_profile_begin", "ea_profile_end",
            "ea_profile_query", "ea_kernel_name")
@@ -164,6 +167,26 @@ def ea_attn_fwd(q, k, v, o, lse, q_seg, k_seg, causal=True, scale=None, stream=N
                            qbr, kbr, qs, nq, ks, nk, EA_MASK_CAUSAL if causal else EA_MASK_FULL, scale,
                            _stream(stream))
     _check(st, "ea_attn_fwd")
+
+
+def ea_attn_fwd_merge(q, k, v, o_acc, lse_acc, q_seg, k_seg, causal=True, scale=None, stream=None):
+    """Forward of q against k/v merged in place into the fp32 accumulator (o_acc [B,Sq,H,D], lse_acc [B,Sq,H])."""
+    import torch
+    _require_bf16(q, k, v)
+    if o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32:
+        raise TypeError("o_acc and lse_acc must be float32")
+    B, sq, H, D = q.shape
+    sk = k.shape[1]
+    qbr, kbr = _rows(q, H, D), _rows(k, H, D)
+    if _rows(v, H, D) != kbr or _rows(o_acc, H, D) != qbr or _stat_rows(lse_acc, H) != qbr or v.shape[1] != sk:
+        raise ValueError("q/o_acc/lse_acc and k/v must share shapes and batch row strides")
+    scale = D ** -0.5 if scale is None else float(scale)
+    qs, nq = _segs(q_seg)
+    ks, nk = _segs(k_seg)
+    st = lib().ea_attn_fwd_merge(_ptr(q), _ptr(k), _ptr(v), _ptr(o_acc), _ptr(lse_acc), B, H, sq, sk, D,
+                                 qbr, kbr, qs, nq, ks, nk, EA_MASK_CAUSAL if causal else EA_MASK_FULL, scale,
+                                 _stream(stream))
+    _check(st, "ea_attn_fwd_merge")
 
 
 def ea_attn_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, q_seg, k_seg, causal=True, scale=None,

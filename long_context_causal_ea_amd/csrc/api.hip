@@ -207,9 +207,10 @@ int ea_zigzag_segments(int64_t s_total, int world, int rank, int64_t* seg_out) {
   return EA_OK;
 }
 
-int ea_attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, int B, int H,
-                int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
-                int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, void* stream) {
+static int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, int B, int H,
+                    int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
+                    int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, int merge,
+                    void* stream) {
   int st = check_common(B, H, Sq, Sk, D, q_batch_rows, k_batch_rows, mask_mode, scale);
   if (st) return st;
   if (o_dtype != EA_F32 && o_dtype != EA_BF16) return EA_ERR_UNSUPPORTED;
@@ -245,10 +246,26 @@ int ea_attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtyp
   a.k_batch_rows = k_batch_rows;
   a.causal = mask_mode == EA_MASK_CAUSAL;
   a.o_bf16 = o_dtype == EA_BF16;
+  a.merge = merge;
   a.scale = scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = timed_launch(EA_KERNEL_FWD, s, [&] { return ea::launch_fwd(a, s); });
   return e == hipSuccess ? EA_OK : hip_fail(e);
+}
+
+int ea_attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, int B, int H,
+                int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
+                int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, void* stream) {
+  return attn_fwd(q, k, v, o, o_dtype, lse, B, H, Sq, Sk, D, q_batch_rows, k_batch_rows, q_seg, n_qseg, k_seg,
+                  n_kseg, mask_mode, scale, 0, stream);
+}
+
+int ea_attn_fwd_merge(const void* q, const void* k, const void* v, float* o_acc, float* lse_acc, int B, int H,
+                      int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows,
+                      const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode,
+                      float scale, void* stream) {
+  return attn_fwd(q, k, v, o_acc, EA_F32, lse_acc, B, H, Sq, Sk, D, q_batch_rows, k_batch_rows, q_seg, n_qseg,
+                  k_seg, n_kseg, mask_mode, scale, 1, stream);
 }
 
 int ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dout,

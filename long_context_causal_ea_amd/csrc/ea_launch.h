@@ -23,6 +23,7 @@ struct FwdArgs {
   SegArg qs, ks;
   int causal;
   int o_bf16;
+  int merge;  // 1: merge into (o, lse) as an fp32 accumulator instead of overwriting
   float scale;
 };
 

@@ -41,7 +41,7 @@ struct FwdParams {
   long rs;                                 // row stride (H*D elements)
   int H, Sq, Sk, nqb;
   Seg qs, ks;
-  int causal, o_bf16;
+  int causal, o_bf16, merge;
   float scale, c;  // c = scale * log2(e)
 };
 
@@ -318,6 +318,31 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   if (!row_ok) return;
   const bool has = lt > 0.f;
   const float inv = has ? 1.f / lt : 0.f;
+  const long lse_at = b * p.lse_bstride + (long)qrow * p.H + h;
+  if (p.merge) {
+    // merge this partial (O = oacc / lt, LSE) into the fp32 accumulator (o, lse):
+    // the log-sum-exp of the two LSEs and the LSE-weighted sum of the two Os,
+    // a side at -inf contributing nothing (the same arithmetic as merge_kernel)
+    float* op = static_cast<float*>(p.o) + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs;
+    const float l1 = p.lse[lse_at];
+    const float l2 = has ? (m_run * p.scale + logf(lt)) : NEG_INF;
+    const float mx = fmaxf(l1, l2), mn = fminf(l1, l2);
+    const float L = (mx == NEG_INF) ? NEG_INF : mx + log1pf(expf(mn - mx));
+    const float w1 = (L == NEG_INF) ? 0.f : expf(l1 - L);
+    const float w2 = (L == NEG_INF) ? 0.f : expf(l2 - L);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * g;
+        f32x4 acc = *reinterpret_cast<const f32x4*>(op + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = w1 * acc[e] + w2 * (oacc[db][4 * q4 + e] * inv);
+        *reinterpret_cast<f32x4*>(op + d0) = acc;
+      }
+    if (g == 0) p.lse[lse_at] = L;
+    return;
+  }
   if (p.o_bf16) {
     uint16_t* op = static_cast<uint16_t*>(p.o) + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs;
 #pragma unroll
@@ -344,7 +369,7 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   }
   if (g == 0) {
     const float lse = has ? (m_run * p.scale + logf(lt)) : NEG_INF;
-    p.lse[b * p.lse_bstride + (long)qrow * p.H + h] = lse;
+    p.lse[lse_at] = lse;
   }
 }
 
@@ -368,6 +393,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.ks = to_seg(a.ks);
   p.causal = a.causal;
   p.o_bf16 = a.o_bf16;
+  p.merge = a.merge;
   p.scale = a.scale;
   p.c = a.scale * kLog2e;
   const int BQ = FwdCfg<128>::BQ;

@@ -153,9 +153,12 @@ class ZigzagRingRank:
     q, do: [B, 2C, H, D] bf16, the rank's local rows (chunk r then chunk 2W-1-r).
     k, v:  [B, W*2C, H, D] bf16, the W ranks' shares side by side: rows
            [2C*s, 2C*(s+1)) are rank s's local keys/values.
+    fused_merge: steps after the first merge their partial result into (o, lse)
+           inside the forward launch (``ea_attn_fwd_merge``); False writes each
+           partial to its own buffers and merges it with ``ea_lse_merge``.
     """
 
-    def __init__(self, q, k, v, world, rank, scale=None, rope_theta=None):
+    def __init__(self, q, k, v, world, rank, scale=None, rope_theta=None, fused_merge=True):
         B, sq, H, D = q.shape
         if sq % 2 or k.shape[1] != world * sq:
             raise ValueError("q must hold 2C rows and k/v W*2C rows")
@@ -173,8 +176,10 @@ class ZigzagRingRank:
         dev = q.device
         self.o = torch.empty((B, sq, H, D), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, sq, H), dtype=torch.float32, device=dev)
-        self.o_part = torch.empty_like(self.o)
-        self.lse_part = torch.empty_like(self.lse)
+        self.fused_merge = fused_merge
+        if not fused_merge:
+            self.o_part = torch.empty_like(self.o)
+            self.lse_part = torch.empty_like(self.lse)
         self.delta = torch.empty_like(self.lse)
         self.dq = torch.empty_like(self.o)
         self.dk = torch.empty((B, k.shape[1], H, D), dtype=torch.float32, device=dev)
@@ -206,6 +211,9 @@ class ZigzagRingRank:
             if t == 0:
                 L.ea_attn_fwd(self.q, kb, vb, self.o, self.lse, self.q_seg, self.k_segs[t], True, self.scale,
                               stream)
+            elif self.fused_merge:
+                L.ea_attn_fwd_merge(self.q, kb, vb, self.o, self.lse, self.q_seg, self.k_segs[t], True,
+                                    self.scale, stream)
             else:
                 L.ea_attn_fwd(self.q, kb, vb, self.o_part, self.lse_part, self.q_seg, self.k_segs[t], True,
                               self.scale, stream)

@@ -79,6 +79,33 @@ def test_fwd_empty_query_is_a_noop_without_pointers():
     assert _fwd(Sq=0, qseg=(0, 0), q=0, o=0, lse=0) == OK
 
 
+def _fwd_merge(**kw):
+    a = dict(q=P, k=P + STEP, v=P + 2 * STEP, o=P + 3 * STEP, lse=P + 4 * STEP, B=1, H=2, Sq=128, Sk=128, D=128,
+             qbr=128, kbr=128, qseg=(0, 128), kseg=(0, 128), mask=1, scale=0.088)
+    a.update(kw)
+    qs, nq = _seg(*a["qseg"])
+    ks, nk = _seg(*a["kseg"])
+    vp = ctypes.c_void_p
+    return ea.lib().ea_attn_fwd_merge(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), vp(a["lse"]), a["B"],
+                                      a["H"], a["Sq"], a["Sk"], a["D"], a["qbr"], a["kbr"], qs, nq, ks, nk,
+                                      a["mask"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), NULL), (dict(o=0), NULL), (dict(lse=0), NULL), (dict(k=0), NULL),
+    (dict(B=0), SHAPE), (dict(B=2, qbr=100), SHAPE), (dict(D=96), UNSUP), (dict(mask=3), UNSUP),
+    (dict(scale=0.0), UNSUP), (dict(qseg=(0, 100)), POS), (dict(kseg=((1 << 31) - 10, 128)), POS),
+    (dict(o=P + 3 * STEP + 4), ALIGN), (dict(lse=P + 4 * STEP + 2), ALIGN),
+    (dict(o=P), ALIAS), (dict(lse=P + 2 * STEP + 64), ALIAS), (dict(lse=P + 3 * STEP + 16), ALIAS),
+])
+def test_fwd_merge_rejects_bad_arguments(kw, code):
+    assert _fwd_merge(**kw) == code
+
+
+def test_fwd_merge_empty_query_is_a_noop_without_pointers():
+    assert _fwd_merge(Sq=0, qseg=(0, 0), q=0, o=0, lse=0) == OK
+
+
 def _bwd(**kw):
     a = dict(q=P, k=P + STEP, v=P + 2 * STEP, o=P + 3 * STEP, o_dtype=0, do=P + 4 * STEP, lse=P + 5 * STEP,
              delta=P + 6 * STEP, ready=0, dq=P + 7 * STEP, dk=P + 8 * STEP, dv=P + 9 * STEP, B=1, H=2, Sq=128,

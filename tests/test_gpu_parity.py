@@ -192,6 +192,66 @@ def test_merge_against_oracle():
     assert_lse("LSE(bf16 part)", la2, ref_l2, tol=1e-5)
 
 
+MERGE_CASES = [
+    # D, B, q_seg, first key segment, merged key segment, causal
+    (128, 1, [0, 300], [0, 150], [150, 150], True),     # rows < 150 see nothing in the merged call
+    (128, 1, [0, 300], [150, 150], [0, 150], True),     # rows < 150 start from an empty accumulator
+    (64, 2, [0, 200], [0, 90, 500, 40], [90, 110], False),
+    (128, 1, [0, 130], [200, 77], [300, 64], True),      # no key for any row in either call
+    (128, 1, [40, 257], [0, 100], [100, 0], True),       # empty merged call
+    (128, 1, [2 ** 31 - 300, 300], [2 ** 31 - 700, 400], [2 ** 31 - 300, 300], True),
+]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES, ids=[f"case{i}" for i in range(len(MERGE_CASES))])
+def test_fwd_merge(case):
+    """ea_attn_fwd_merge against ea_attn_fwd into a partial followed by ea_lse_merge (the same arithmetic, so
+    to within a few fp32 roundings), and both key sets together against the oracle's attention over their union."""
+    D, B, q_seg, ka_seg, kb_seg, causal = case
+    H = 2
+    sq, ska, skb = sum(q_seg[1::2]), sum(ka_seg[1::2]), sum(kb_seg[1::2])
+    banner(f"fwd_merge D={D} B={B} q_seg={q_seg} first={ka_seg} merged={kb_seg} causal={causal}")
+    q = _rand((B, sq, H, D), 810)
+    ka, va = _rand((B, ska, H, D), 811), _rand((B, ska, H, D), 812)
+    kb, vb = _rand((B, skb, H, D), 813), _rand((B, skb, H, D), 814)
+    of, lf = torch.empty((B, sq, H, D), device=DEV), torch.empty((B, sq, H), device=DEV)
+    ea.ea_attn_fwd(q, ka, va, of, lf, q_seg, ka_seg, causal)
+    first_o, first_l = of.clone(), lf.clone()
+    ea.ea_attn_fwd_merge(q, kb, vb, of, lf, q_seg, kb_seg, causal)
+    osep, lsep = first_o.clone(), first_l.clone()
+    op, lp = torch.empty_like(osep), torch.empty_like(lsep)
+    ea.ea_attn_fwd(q, kb, vb, op, lp, q_seg, kb_seg, causal)
+    ea.ea_lse_merge(osep, lsep, op, lp)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.isneginf(lf), torch.isneginf(lsep))
+    fin = ~torch.isneginf(lsep)
+    if bool(fin.any()):
+        assert float((lf[fin] - lsep[fin]).abs().max()) <= 1e-6
+    assert float((of - osep).abs().max()) <= 1e-6
+    if skb == 0:  # an empty merged call leaves the accumulator as it was
+        assert torch.equal(of, first_o) and torch.equal(lf, first_l)
+    k_all, v_all = torch.cat([ka, kb], dim=1), torch.cat([va, vb], dim=1)
+    pk = np.concatenate([seg_positions(ka_seg), seg_positions(kb_seg)])
+    ref_o, ref_l = oracle.attn_fwd_heads(q, k_all, v_all, seg_positions(q_seg), pk, causal, scale_of(D))
+    assert_close("O", of, ref_o)
+    assert_lse("LSE", lf, ref_l)
+
+
+def test_ring_fused_and_separate_merge_agree():
+    W, C, H, D, rank = 4, 70, 2, 128, 1
+    banner(f"zigzag ring fused vs separate merge W={W} C={C} rank={rank}")
+    t = {n: _rand((1, s, H, D), 830 + i) for i, (n, s) in
+         enumerate((("q", 2 * C), ("k", 2 * W * C), ("v", 2 * W * C), ("do", 2 * C)))}
+    fused = ea.ZigzagRingRank(t["q"], t["k"], t["v"], W, rank)
+    sep = ea.ZigzagRingRank(t["q"], t["k"], t["v"], W, rank, fused_merge=False)
+    fused.step(t["do"])
+    sep.step(t["do"])
+    torch.cuda.synchronize()
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        a, b = getattr(fused, n), getattr(sep, n)
+        assert float((a - b).abs().max()) <= 1e-5 * max(1.0, float(b.abs().max())), n
+
+
 @pytest.mark.parametrize("rank", [0, 3, 7])
 @pytest.mark.parametrize("C,D", [(100, 128), (64, 64), (37, 128)])
 def test_zigzag_ring_small(rank, C, D):
