@@ -73,7 +73,8 @@ enum ea_status {
   EA_ERR_POSITIONS = 4,    /* bad segment count, lengths, starts or positions >= 2^31 */
   EA_ERR_ALIGN = 5,        /* pointer misaligned */
   EA_ERR_ALIAS = 6,        /* an output overlaps an input */
-  EA_ERR_HIP = 7           /* a HIP launch failed */
+  EA_ERR_HIP = 7,          /* a HIP launch failed */
+  EA_ERR_WORKSPACE = 8     /* workspace smaller than one (batch, head) needs */
 };
 
 enum ea_mask { EA_MASK_FULL = 0, EA_MASK_CAUSAL = 1 };
@@ -140,6 +141,40 @@ int ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, int 
                 int64_t q_batch_rows, int64_t k_batch_rows,
                 const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg,
                 int mask_mode, float scale, void* stream);
+
+/*
+ * The same backward (same arguments, results and errors) with dS kept in a
+ * caller-provided device workspace instead of recomputed.  The key-major pass
+ * forms dS = P (dP - Delta) for each key block anyway; here it also writes it,
+ * rounded to bf16 (the value the dk product uses), into the workspace, and the
+ * dq pass becomes one contraction dq_i += scale * sum_j dS_ij k_j that reads it
+ * back, in place of recomputing the scores and dP of every allowed pair.  The
+ * panel holds one 16 KiB block per (256-query block, 32-key group) with any
+ * allowed pair; ea_attn_bwd_ws_bytes gives its size for one (batch, head).
+ * Heads are processed in groups of floor(ws_bytes / that size) (all B*H at once
+ * if they fit), each group's two passes before the next group's.
+ * workspace: device memory, 16-byte aligned, overlapping no other argument,
+ * owned by the caller, contents undefined on entry and on return; calls that
+ * share a workspace must be ordered on one stream.  Returns EA_ERR_WORKSPACE if
+ * ws_bytes is below the size of one (batch, head), EA_ERR_NULL for a NULL
+ * workspace when one is needed, otherwise as ea_attn_bwd.
+ */
+int ea_attn_bwd_ws(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                   const void* dout, const float* lse, float* delta, int delta_ready,
+                   float* dq, float* dk, float* dv,
+                   int B, int H, int64_t Sq, int64_t Sk, int D,
+                   int64_t q_batch_rows, int64_t k_batch_rows,
+                   const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg,
+                   int mask_mode, float scale, void* workspace, int64_t ws_bytes, void* stream);
+
+/*
+ * Bytes of dS panel one (batch, head) of ea_attn_bwd_ws needs for these
+ * segments and mask (host only; no HIP call).  Writes *bytes_per_head and
+ * returns EA_OK, or EA_ERR_NULL / EA_ERR_POSITIONS / EA_ERR_UNSUPPORTED /
+ * EA_ERR_SHAPE (a panel of 2^31 blocks or more) for bad arguments.
+ */
+int ea_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, const int64_t* q_seg, int n_qseg, const int64_t* k_seg,
+                         int n_kseg, int mask_mode, int64_t* bytes_per_head);
 
 /*
  * In-place LSE merge of a partial result over a disjoint key set into an
@@ -236,7 +271,8 @@ enum ea_kernel {
   EA_KERNEL_LSE_MERGE = 4,
   EA_KERNEL_XENT = 5,
   EA_KERNEL_ROPE = 6,
-  EA_KERNEL_COUNT = 7
+  EA_KERNEL_BWD_DQ_PANEL = 7,  /* dq from the dS panel (ea_attn_bwd_ws) */
+  EA_KERNEL_COUNT = 8
 };
 int ea_profile_begin(void);
 int ea_profile_end(void);

@@ -7,7 +7,7 @@ position, and the fused cross-entropy of the training step.  PyTorch supplies
 device memory and streams only.
 """
 from ._lib import (  # noqa: F401
-    EA_BF16, EA_F32, EA_MASK_CAUSAL, EA_MASK_FULL, EaError, EXPORTS, KERNELS, LIB_PATH, ea_attn_bwd, ea_attn_fwd,
+    EA_BF16, EA_F32, EA_MASK_CAUSAL, EA_MASK_FULL, EaError, EXPORTS, KERNELS, LIB_PATH, ea_attn_bwd, ea_attn_bwd_ws_bytes, ea_attn_fwd,
     ea_attn_fwd_merge,
     ea_kernel_name, ea_lse_merge, ea_profile_begin, ea_profile_end, ea_profile_query, ea_ring_source, ea_rope,
     ea_version, ea_xent_fwd_bwd, ea_zigzag_segments, lib, strerror,

@@ -48,6 +48,11 @@ def lib():
     L.ea_attn_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, i32, i32, i64, i64, i32,
                               i64, i64, pi64, i32, pi64, i32, i32, f32, vp]
     L.ea_attn_bwd.restype = i32
+    L.ea_attn_bwd_ws.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, i32, i32, i64, i64, i32,
+                                 i64, i64, pi64, i32, pi64, i32, i32, f32, vp, i64, vp]
+    L.ea_attn_bwd_ws.restype = i32
+    L.ea_attn_bwd_ws_bytes.argtypes = [i64, i64, pi64, i32, pi64, i32, i32, pi64]
+    L.ea_attn_bwd_ws_bytes.restype = i32
     L.ea_lse_merge.argtypes = [vp, vp, vp, i32, vp, i32, i32, i64, i32, i64, vp]
     L.ea_lse_merge.restype = i32
     L.ea_xent_fwd_bwd.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, i64, f32, vp]
@@ -76,12 +81,12 @@ def lib():
     return L
 
 
-EXPORTS = ("ea_attn_fwd", "ea_attn_fwd_merge", "ea_attn_bwd", "ea_lse_merge", "ea_xent_fwd_bwd", "ea_rope", "ea_zigzag_segments",
+EXPORTS = ("ea_attn_fwd", "ea_attn_fwd_merge", "ea_attn_bwd", "ea_attn_bwd_ws", "ea_attn_bwd_ws_bytes", "ea_lse_merge", "ea_xent_fwd_bwd", "ea_rope", "ea_zigzag_segments",
            "ea_ring_source",
            "ea_strerror", "ea_last_hip_error", "ea_version", "ea_profile_begin", "ea_profile_end",
            "ea_profile_query", "ea_kernel_name")
 
-KERNELS = ("fwd", "bwd_delta", "bwd_dkdv", "bwd_dq", "lse_merge", "xent", "rope")
+KERNELS = ("fwd", "bwd_delta", "bwd_dkdv", "bwd_dq", "lse_merge", "xent", "rope", "bwd_dq_panel")
 
 
 def strerror(status: int) -> str:
@@ -190,8 +195,12 @@ def ea_attn_fwd_merge(q, k, v, o_acc, lse_acc, q_seg, k_seg, causal=True, scale=
 
 
 def ea_attn_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, q_seg, k_seg, causal=True, scale=None,
-                delta_ready=False, stream=None):
-    """Accumulates dq, dk, dv (fp32) for the final (o, lse); writes delta unless delta_ready."""
+                delta_ready=False, stream=None, workspace=None):
+    """Accumulates dq, dk, dv (fp32) for the final (o, lse); writes delta unless delta_ready.
+
+    workspace: None recomputes the scores for dq (``ea_attn_bwd``); a device tensor (any dtype, contiguous)
+    keeps the bf16 dS panel there and computes dq from it (``ea_attn_bwd_ws``; size per (batch, head) from
+    ``ea_attn_bwd_ws_bytes``)."""
     _require_bf16(q, k, v, dout)
     B, sq, H, D = q.shape
     sk = k.shape[1]
@@ -206,11 +215,28 @@ def ea_attn_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, q_seg, k_seg, causal=T
     scale = D ** -0.5 if scale is None else float(scale)
     qs, nq = _segs(q_seg)
     ks, nk = _segs(k_seg)
-    st = lib().ea_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o) if o is not None else EA_F32,
-                           _ptr(dout), _ptr(lse), _ptr(delta), 1 if delta_ready else 0, _ptr(dq), _ptr(dk),
-                           _ptr(dv), B, H, sq, sk, D, qbr, kbr, qs, nq, ks, nk,
-                           EA_MASK_CAUSAL if causal else EA_MASK_FULL, scale, _stream(stream))
-    _check(st, "ea_attn_bwd")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o) if o is not None else EA_F32,
+            _ptr(dout), _ptr(lse), _ptr(delta), 1 if delta_ready else 0, _ptr(dq), _ptr(dk),
+            _ptr(dv), B, H, sq, sk, D, qbr, kbr, qs, nq, ks, nk,
+            EA_MASK_CAUSAL if causal else EA_MASK_FULL, scale)
+    if workspace is None:
+        _check(lib().ea_attn_bwd(*args, _stream(stream)), "ea_attn_bwd")
+        return
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().ea_attn_bwd_ws(*args, _ptr(workspace), nbytes, _stream(stream)), "ea_attn_bwd_ws")
+
+
+def ea_attn_bwd_ws_bytes(sq: int, sk: int, q_seg, k_seg, causal=True) -> int:
+    """Bytes of dS panel one (batch, head) of ``ea_attn_bwd_ws`` needs."""
+    qs, nq = _segs(q_seg)
+    ks, nk = _segs(k_seg)
+    out = ctypes.c_int64(0)
+    st = lib().ea_attn_bwd_ws_bytes(int(sq), int(sk), qs, nq, ks, nk, EA_MASK_CAUSAL if causal else EA_MASK_FULL,
+                                    ctypes.byref(out))
+    _check(st, "ea_attn_bwd_ws_bytes")
+    return int(out.value)
 
 
 def ea_lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):

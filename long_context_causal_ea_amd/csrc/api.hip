@@ -133,6 +133,7 @@ const char* ea_strerror(int status) {
     case EA_ERR_ALIGN: return "pointer misaligned (the alignment each call documents in ea_attn.h)";
     case EA_ERR_ALIAS: return "an output buffer overlaps an input buffer";
     case EA_ERR_HIP: return "a HIP launch failed (see ea_last_hip_error)";
+    case EA_ERR_WORKSPACE: return "workspace smaller than one (batch, head) of the dS panel needs";
     default: return "unknown status";
   }
 }
@@ -186,6 +187,7 @@ const char* ea_kernel_name(int kernel) {
     case EA_KERNEL_LSE_MERGE: return "lse_merge";
     case EA_KERNEL_XENT: return "xent";
     case EA_KERNEL_ROPE: return "rope";
+    case EA_KERNEL_BWD_DQ_PANEL: return "bwd_dq_panel";
     default: return "unknown";
   }
 }
@@ -268,10 +270,19 @@ int ea_attn_fwd_merge(const void* q, const void* k, const void* v, float* o_acc,
                   k_seg, n_kseg, mask_mode, scale, 1, stream);
 }
 
-int ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dout,
-                const float* lse, float* delta, int delta_ready, float* dq, float* dk, float* dv, int B, int H,
-                int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
-                int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kPanelBlockBytes = (int64_t)256 * 32 * 2;  // one (256-query, 32-key) bf16 block
+
+// use_ws == 0: dq by recomputation (ea_attn_bwd); 1: dq from the dS panel in
+// the workspace (ea_attn_bwd_ws).
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dout,
+             const float* lse, float* delta, int delta_ready, float* dq, float* dk, float* dv, int B, int H,
+             int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
+             int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, int use_ws, void* ws,
+             int64_t ws_bytes, void* stream) {
   int st = check_common(B, H, Sq, Sk, D, q_batch_rows, k_batch_rows, mask_mode, scale);
   if (st) return st;
   if (o_dtype != EA_F32 && o_dtype != EA_BF16) return EA_ERR_UNSUPPORTED;
@@ -301,6 +312,19 @@ int ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, int 
   if (overlap(sdq, sdk) || overlap(sdq, sdv) || overlap(sdk, sdv) || overlap(sdl, sdq) || overlap(sdl, sdk) ||
       overlap(sdl, sdv))
     return EA_ERR_ALIAS;
+  int64_t per_bh = 0;  // panel blocks per (batch, head)
+  if (use_ws && Sk > 0) {
+    per_bh = ea::panel_blocks(a.qs, a.ks, mask_mode == EA_MASK_CAUSAL);
+    if (per_bh >= kPosLimit) return EA_ERR_SHAPE;
+    if (per_bh > 0) {
+      if (!ws) return EA_ERR_NULL;
+      if (!aligned(ws, 16)) return EA_ERR_ALIGN;
+      if (ws_bytes < per_bh * kPanelBlockBytes) return EA_ERR_WORKSPACE;
+      const Span sw{(uintptr_t)ws, (uintptr_t)ws + (uintptr_t)ws_bytes};
+      for (const Span& x : {sq, sk, sv, sdo, sl, so, sdl, sdq, sdk, sdv})
+        if (overlap(sw, x)) return EA_ERR_ALIAS;
+    }
+  }
 
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -322,15 +346,92 @@ int ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, int 
   a.causal = mask_mode == EA_MASK_CAUSAL;
   a.o_bf16 = o_dtype == EA_BF16;
   a.scale = scale;
+  a.Hs = H;
+  a.ds = nullptr;
+  a.ds_per_bh = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (!delta_ready) e = timed_launch(EA_KERNEL_BWD_DELTA, s, [&] { return ea::launch_bwd_delta(a, s); });
   if (e != hipSuccess) return hip_fail(e);
   if (Sk == 0) return EA_OK;
-  e = timed_launch(EA_KERNEL_BWD_DKDV, s, [&] { return ea::launch_bwd_dkdv(a, s); });
-  if (e != hipSuccess) return hip_fail(e);
-  e = timed_launch(EA_KERNEL_BWD_DQ, s, [&] { return ea::launch_bwd_dq(a, s); });
-  return e == hipSuccess ? EA_OK : hip_fail(e);
+  if (!use_ws) {
+    e = timed_launch(EA_KERNEL_BWD_DKDV, s, [&] { return ea::launch_bwd_dkdv(a, s); });
+    if (e != hipSuccess) return hip_fail(e);
+    e = timed_launch(EA_KERNEL_BWD_DQ, s, [&] { return ea::launch_bwd_dq(a, s); });
+    return e == hipSuccess ? EA_OK : hip_fail(e);
+  }
+  if (per_bh == 0) return EA_OK;  // no allowed pair anywhere: nothing to accumulate
+  // groups of heads whose panels fit the workspace, each group's two passes in turn
+  const int64_t cap = ws_bytes / (per_bh * kPanelBlockBytes);
+  a.ds = static_cast<uint16_t*>(ws);
+  a.ds_per_bh = (int)per_bh;
+  auto run = [&](const ea::BwdArgs& g) {
+    hipError_t r = timed_launch(EA_KERNEL_BWD_DKDV, s, [&] { return ea::launch_bwd_dkdv(g, s); });
+    if (r != hipSuccess) return r;
+    return timed_launch(EA_KERNEL_BWD_DQ_PANEL, s, [&] { return ea::launch_bwd_dqs(g, s); });
+  };
+  if (cap >= (int64_t)B * H) {
+    e = run(a);
+    return e == hipSuccess ? EA_OK : hip_fail(e);
+  }
+  const int G = (int)(cap < H ? cap : H);
+  for (int b = 0; b < B; ++b)
+    for (int h0 = 0; h0 < H; h0 += G) {
+      ea::BwdArgs g = a;
+      const int64_t tok = (int64_t)b * q_batch_rows * H * D + (int64_t)h0 * D;
+      const int64_t ktok = (int64_t)b * k_batch_rows * H * D + (int64_t)h0 * D;
+      const int64_t row = (int64_t)b * q_batch_rows * H + h0;
+      g.B = 1;
+      g.H = H - h0 < G ? H - h0 : G;
+      g.q = a.q + tok;
+      g.dout = a.dout + tok;
+      g.dq = a.dq + tok;
+      g.k = a.k + ktok;
+      g.v = a.v + ktok;
+      g.dk = a.dk + ktok;
+      g.dv = a.dv + ktok;
+      g.lse = a.lse + row;
+      g.delta = a.delta + row;
+      e = run(g);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+  return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dout,
+                const float* lse, float* delta, int delta_ready, float* dq, float* dk, float* dv, int B, int H,
+                int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
+                int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, void* stream) {
+  return attn_bwd(q, k, v, o, o_dtype, dout, lse, delta, delta_ready, dq, dk, dv, B, H, Sq, Sk, D, q_batch_rows,
+                  k_batch_rows, q_seg, n_qseg, k_seg, n_kseg, mask_mode, scale, 0, nullptr, 0, stream);
+}
+
+int ea_attn_bwd_ws(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dout,
+                   const float* lse, float* delta, int delta_ready, float* dq, float* dk, float* dv, int B, int H,
+                   int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
+                   int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, void* workspace,
+                   int64_t ws_bytes, void* stream) {
+  return attn_bwd(q, k, v, o, o_dtype, dout, lse, delta, delta_ready, dq, dk, dv, B, H, Sq, Sk, D, q_batch_rows,
+                  k_batch_rows, q_seg, n_qseg, k_seg, n_kseg, mask_mode, scale, 1, workspace, ws_bytes, stream);
+}
+
+int ea_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, const int64_t* q_seg, int n_qseg, const int64_t* k_seg,
+                         int n_kseg, int mask_mode, int64_t* bytes_per_head) {
+  if (!bytes_per_head) return EA_ERR_NULL;
+  if (Sq < 0 || Sk < 0 || Sq >= kPosLimit || Sk >= kPosLimit) return EA_ERR_SHAPE;
+  if (mask_mode != EA_MASK_FULL && mask_mode != EA_MASK_CAUSAL) return EA_ERR_UNSUPPORTED;
+  SegArg qs, ks;
+  int st;
+  if ((st = check_segs(q_seg, n_qseg, Sq, &qs))) return st;
+  if ((st = check_segs(k_seg, n_kseg, Sk, &ks))) return st;
+  const int64_t n = (Sq == 0 || Sk == 0) ? 0 : ea::panel_blocks(qs, ks, mask_mode == EA_MASK_CAUSAL);
+  if (n >= kPosLimit) return EA_ERR_SHAPE;
+  *bytes_per_head = n * kPanelBlockBytes;
+  return EA_OK;
 }
 
 int ea_lse_merge(float* o_acc, float* lse_acc, const void* o_part, int part_dtype, const float* lse_part, int B,

@@ -148,7 +148,7 @@ struct Seg {
 __device__ __forceinline__ int seg_pos(const Seg& g, int i) { return i < g.l0 ? g.s0 + i : g.s1 + (i - g.l0); }
 
 // Smallest and largest position among rows [a, b) (a < b <= n).
-__device__ __forceinline__ void seg_range(const Seg& g, int a, int b, int& mn, int& mx) {
+__host__ __device__ __forceinline__ void seg_range(const Seg& g, int a, int b, int& mn, int& mx) {
   mn = 0x7fffffff;
   mx = -1;
   if (a < g.l0) {
@@ -166,7 +166,7 @@ __device__ __forceinline__ void seg_range(const Seg& g, int a, int b, int& mn, i
 
 // Key rows that any query with position <= qmax may see under the causal rule,
 // as up to two row ranges [0, e0) and [b1, e1) of the key tensor.
-__device__ __forceinline__ void causal_key_ranges(const Seg& k, int qmax, int& e0, int& b1, int& e1) {
+__host__ __device__ __forceinline__ void causal_key_ranges(const Seg& k, int qmax, int& e0, int& b1, int& e1) {
   long n0 = (long)qmax - k.s0 + 1;
   n0 = n0 < 0 ? 0 : (n0 > k.l0 ? k.l0 : n0);
   e0 = (int)n0;
@@ -175,6 +175,68 @@ __device__ __forceinline__ void causal_key_ranges(const Seg& k, int qmax, int& e
   n1 = n1 < 0 ? 0 : (n1 > len1 ? len1 : n1);
   b1 = k.l0;
   e1 = k.l0 + (int)n1;
+}
+
+// ---- dS panel: the bf16 dS of one backward call, kept in HBM between the
+// key-major pass that forms it and the query-major pass that contracts it with
+// K.  Per (batch, head) it holds one 16 KiB block for every pair (query block of
+// kPanelQ rows, key group of kPanelK keys) the query block may see, query
+// blocks in order; within a query block the key groups come in the order the
+// query-major pass visits them: the groups covering [0, e0), then those
+// covering [b1, e1) not already counted (causal_key_ranges of the block's
+// largest position; every group under the full mask).  A block is eight 2 KiB
+// sub-blocks, one per 32-query tile of the query block, each holding the tile's
+// dS for the group's 32 keys in the order the key-major pass produces it (see
+// the dK/dV kernel); the dQ pass gathers it into row-major tiles.
+constexpr int kPanelQ = 256, kPanelK = 32;
+constexpr long kPanelBlock = (long)kPanelQ * kPanelK;  // elements per block
+
+struct PanelList {
+  int nA, tB0, nB;  // groups [0, nA), then [tB0, tB0 + nB)
+};
+
+__host__ __device__ __forceinline__ PanelList panel_list(const Seg& qs, const Seg& ks, int causal, int qb) {
+  int e0 = ks.n, b1 = ks.n, e1 = ks.n;
+  if (causal) {
+    const int i0 = qb * kPanelQ, i1 = i0 + kPanelQ < qs.n ? i0 + kPanelQ : qs.n;
+    int mn, mx;
+    seg_range(qs, i0, i1, mn, mx);
+    causal_key_ranges(ks, mx, e0, b1, e1);
+  }
+  PanelList L;
+  L.nA = (e0 + kPanelK - 1) / kPanelK;
+  int t0 = b1 / kPanelK, t1 = (e1 + kPanelK - 1) / kPanelK;
+  if (e1 <= b1) t1 = t0;
+  if (t0 < L.nA) t0 = L.nA;
+  L.tB0 = t0;
+  L.nB = t1 > t0 ? t1 - t0 : 0;
+  return L;
+}
+
+__host__ __device__ __forceinline__ int panel_count(const Seg& qs, const Seg& ks, int causal, int qb) {
+  const PanelList L = panel_list(qs, ks, causal, qb);
+  return L.nA + L.nB;
+}
+
+// Index of key group kg in a query block's list, or -1 if the block sees none
+// of its keys.
+__host__ __device__ __forceinline__ int panel_pos(const PanelList& L, int kg) {
+  if (kg < L.nA) return kg;
+  const int u = kg - L.tB0;
+  return (u >= 0 && u < L.nB) ? L.nA + u : -1;
+}
+
+// Blocks of query blocks [0, qb) of one (batch, head), summed by the 64 lanes
+// of a wave (all lanes must be active; the result is uniform).
+__device__ __forceinline__ int panel_prefix(const Seg& qs, const Seg& ks, int causal, int qb, int lane) {
+  int s = 0;
+  for (int q0 = 0; q0 < qb; q0 += 64) {
+    const int q = q0 + lane;
+    if (q < qb) s += panel_count(qs, ks, causal, q);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  return __builtin_amdgcn_readfirstlane(s);
 }
 
 // Key rows a query at position qpos may see, as [0, lim0) U [l0, lim1) of the

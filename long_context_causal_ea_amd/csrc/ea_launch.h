@@ -39,11 +39,14 @@ struct BwdArgs {
   float* dk;
   float* dv;
   int B, H, D, Sq, Sk;
+  int Hs;  // heads per token row (the row stride); H of them, from the pointers on, are processed
   int64_t q_batch_rows, k_batch_rows;
   SegArg qs, ks;
   int causal;
   int o_bf16;
   float scale;
+  uint16_t* ds;   // dS panel for these B*H heads, or null (dQ by recomputation)
+  int ds_per_bh;  // panel blocks per (batch, head)
 };
 
 struct MergeArgs {
@@ -83,6 +86,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dqs(const BwdArgs& a, hipStream_t stream);
+// dS panel blocks per (batch, head) for these query/key segments (16 KiB each).
+int64_t panel_blocks(const SegArg& qs, const SegArg& ks, int causal);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_xent(const XentArgs& a, hipStream_t stream);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);

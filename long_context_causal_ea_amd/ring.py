@@ -92,6 +92,17 @@ def _zero(stream, *ts):
             t.zero_()
 
 
+def _panel(dev, per_head: int, heads: int, cap_bytes):
+    """Workspace for the dS panel: all ``heads`` (batch, head) slices if they fit ``cap_bytes``, else as many
+    whole slices as fit (the library then runs the heads in groups); None without a cap (dq by recomputation)."""
+    if cap_bytes is None or per_head == 0:
+        return None
+    n = min(heads, int(cap_bytes) // per_head)
+    if n < 1:
+        raise ValueError(f"panel_bytes {cap_bytes} below one head's dS panel ({per_head} bytes)")
+    return torch.empty(n * per_head, dtype=torch.uint8, device=dev)
+
+
 def capture_step(driver, do):
     """Record one whole ``driver.step(do)`` (rotations, forward, merges, zeroing, backward) as a HIP graph.
 
@@ -106,7 +117,13 @@ def capture_step(driver, do):
 
 
 class DenseCausal:
-    def __init__(self, q, k, v, causal=True, scale=None, o_dtype=torch.float32, rope_theta=None):
+    """Dense (whole-sequence) attention of one GPU: forward, then backward into fp32 gradients.
+
+    panel_bytes: None computes dq by recomputing the scores; a byte count keeps the bf16 dS in a workspace of at
+    most that size (``ea_attn_bwd_ws``), allocated here once.
+    """
+
+    def __init__(self, q, k, v, causal=True, scale=None, o_dtype=torch.float32, rope_theta=None, panel_bytes=None):
         B, S, H, D = q.shape
         self.rope_theta = rope_theta
         self.q_in, self.k_in = q, k
@@ -126,6 +143,8 @@ class DenseCausal:
         self.dv = torch.empty_like(self.dk)
         self.q_seg = [0, S]
         self.k_seg = [0, k.shape[1]]
+        self.panel = _panel(dev, L.ea_attn_bwd_ws_bytes(S, k.shape[1], self.q_seg, self.k_seg, causal), B * H,
+                            panel_bytes)
 
     def forward(self, stream=None):
         if self.rope_theta is not None:
@@ -137,7 +156,8 @@ class DenseCausal:
     def backward(self, do, stream=None):
         _zero(stream, self.dq, self.dk, self.dv)
         L.ea_attn_bwd(self.q, self.k, self.v, self.o, do, self.lse, self.delta, self.dq, self.dk, self.dv,
-                      self.q_seg, self.k_seg, self.causal, self.scale, delta_ready=False, stream=stream)
+                      self.q_seg, self.k_seg, self.causal, self.scale, delta_ready=False, stream=stream,
+                      workspace=self.panel)
         if self.rope_theta is not None:
             L.ea_rope(self.dq, self.dq, self.q_seg, self.rope_theta, inverse=True, stream=stream)
             L.ea_rope(self.dk, self.dk, self.k_seg, self.rope_theta, inverse=True, stream=stream)
@@ -156,9 +176,11 @@ class ZigzagRingRank:
     fused_merge: steps after the first merge their partial result into (o, lse)
            inside the forward launch (``ea_attn_fwd_merge``); False writes each
            partial to its own buffers and merges it with ``ea_lse_merge``.
+    panel_bytes: as for DenseCausal; one workspace serves every ring step (the
+           steps run in order on one stream).
     """
 
-    def __init__(self, q, k, v, world, rank, scale=None, rope_theta=None, fused_merge=True):
+    def __init__(self, q, k, v, world, rank, scale=None, rope_theta=None, fused_merge=True, panel_bytes=None):
         B, sq, H, D = q.shape
         if sq % 2 or k.shape[1] != world * sq:
             raise ValueError("q must hold 2C rows and k/v W*2C rows")
@@ -188,6 +210,8 @@ class ZigzagRingRank:
         self.sources = [L.ea_ring_source(rank, t, world) for t in range(world)]
         self.k_segs = [L.ea_zigzag_segments(self.s_total, world, s) for s in self.sources]
         self.share_segs = [L.ea_zigzag_segments(self.s_total, world, s) for s in range(world)]
+        per_head = max(L.ea_attn_bwd_ws_bytes(sq, sq, self.q_seg, ks, True) for ks in self.k_segs)
+        self.panel = _panel(dev, per_head, B * H, panel_bytes)
 
     def _share(self, s, x):
         return x[:, 2 * self.C * s: 2 * self.C * (s + 1)]
@@ -225,7 +249,7 @@ class ZigzagRingRank:
             kb, vb = self._block(t, self.k), self._block(t, self.v)
             L.ea_attn_bwd(self.q, kb, vb, self.o, do, self.lse, self.delta, self.dq, self._block(t, self.dk),
                           self._block(t, self.dv), self.q_seg, self.k_segs[t], True, self.scale,
-                          delta_ready=(t > 0), stream=stream)
+                          delta_ready=(t > 0), stream=stream, workspace=self.panel)
         if self.rope_theta is not None:
             self._rope_all(self.dq, self.dq, self.dk, self.dk, True, stream)
 

@@ -247,3 +247,94 @@ def test_rope_rejects_bad_arguments(kw, code):
 
 def test_rope_empty_is_noop():
     assert _rope(S=0, br=0, seg=(5, 0), x=0, y=0) == OK
+
+
+# ---- backward with the dS panel in a caller workspace (ea_attn_bwd_ws, ea_attn_bwd_ws_bytes)
+WORKSPACE = 8
+
+
+def _panel_blocks_brute(pos_q, pos_k, causal):
+    """(256-query block, 32-key group) pairs holding at least one allowed pair, counted over positions."""
+    n = 0
+    for i0 in range(0, len(pos_q), 256):
+        qmax = pos_q[i0:i0 + 256].max()
+        for j0 in range(0, len(pos_k), 32):
+            if not causal or pos_k[j0:j0 + 32].min() <= qmax:
+                n += 1
+    return n
+
+
+@pytest.mark.parametrize("sq,sk,q_seg,k_seg,causal", [
+    (512, 512, [0, 512], [0, 512], True),
+    (1000, 1000, [0, 1000], [0, 1000], True),
+    (333, 200, [0, 333], [0, 200], False),
+    (777, 1301, [300, 400, 2000, 377], [0, 650, 1800, 651], True),
+    (190, 190, [0, 190], [100, 190], True),
+    (300, 400, [2 ** 31 - 300, 300], [2 ** 31 - 500, 400], True),
+    (200, 200, [2 ** 31 - 200, 100, 1000, 100], [2 ** 31 - 150, 150, 0, 50], True),
+    (1, 450, [449, 1], [0, 450], True),
+    (450, 1, [0, 450], [5000, 1], True),  # no allowed pair at all
+])
+def test_panel_bytes_match_brute_force(sq, sk, q_seg, k_seg, causal):
+    from tests.parity import seg_positions
+    got = ea.ea_attn_bwd_ws_bytes(sq, sk, q_seg, k_seg, causal)
+    assert got == _panel_blocks_brute(seg_positions(q_seg), seg_positions(k_seg), causal) * 256 * 32 * 2
+
+
+@pytest.mark.parametrize("W,C", [(8, 37), (4, 100), (8, 43750 // 16)])
+def test_panel_bytes_zigzag_steps(W, C):
+    for r in (0, W // 2, W - 1):
+        pq = oracle.zigzag_positions(2 * W * C, W, r)
+        for t in range(W):
+            s = oracle.ring_source(r, t, W)
+            pk = oracle.zigzag_positions(2 * W * C, W, s)
+            got = ea.ea_attn_bwd_ws_bytes(2 * C, 2 * C, ea.ea_zigzag_segments(2 * W * C, W, r),
+                                          ea.ea_zigzag_segments(2 * W * C, W, s), True)
+            assert got == _panel_blocks_brute(pq, pk, True) * 16384, (r, t)
+
+
+def test_panel_bytes_errors():
+    out = ctypes.c_int64(-1)
+    qs, nq = _seg(0, 100)
+    ks, nk = _seg(0, 50)
+    lib = ea.lib()
+    assert lib.ea_attn_bwd_ws_bytes(100, 50, qs, nq, ks, nk, 1, None) == NULL
+    assert lib.ea_attn_bwd_ws_bytes(100, 60, qs, nq, ks, nk, 1, ctypes.byref(out)) == POS
+    assert lib.ea_attn_bwd_ws_bytes(100, 50, qs, nq, ks, nk, 3, ctypes.byref(out)) == UNSUP
+    assert lib.ea_attn_bwd_ws_bytes(-1, 50, qs, nq, ks, nk, 1, ctypes.byref(out)) == SHAPE
+    z, nz = _seg(0, 0)
+    assert lib.ea_attn_bwd_ws_bytes(0, 50, z, nz, ks, nk, 1, ctypes.byref(out)) == OK and out.value == 0
+
+
+WS = P + 10 * STEP
+
+
+def _bwd_ws(ws=WS, ws_bytes=1 << 30, **kw):
+    a = dict(q=P, k=P + STEP, v=P + 2 * STEP, o=P + 3 * STEP, o_dtype=0, do=P + 4 * STEP, lse=P + 5 * STEP,
+             delta=P + 6 * STEP, ready=0, dq=P + 7 * STEP, dk=P + 8 * STEP, dv=P + 9 * STEP, B=1, H=2, Sq=128,
+             Sk=256, D=64, qbr=128, kbr=256, qseg=(0, 128), kseg=(0, 256), mask=1, scale=0.125)
+    a.update(kw)
+    qs, nq = _seg(*a["qseg"])
+    ks, nk = _seg(*a["kseg"])
+    vp = ctypes.c_void_p
+    return ea.lib().ea_attn_bwd_ws(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), a["o_dtype"], vp(a["do"]),
+                                   vp(a["lse"]), vp(a["delta"]), a["ready"], vp(a["dq"]), vp(a["dk"]),
+                                   vp(a["dv"]), a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["qbr"], a["kbr"], qs,
+                                   nq, ks, nk, a["mask"], a["scale"], vp(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws_bytes=16384 * 4 - 16), WORKSPACE),   # one (batch, head) needs 4 blocks here (keys 0..127)
+    (dict(ws_bytes=0), WORKSPACE),
+    (dict(ws=0), NULL),
+    (dict(ws=WS + 8), ALIGN),
+    (dict(ws=P + 7 * STEP - 4096), ALIAS),          # runs into dq
+    (dict(ws=P + 2 * STEP), ALIAS),                 # over v
+    (dict(q=0), NULL), (dict(D=32), UNSUP), (dict(kseg=(0, 255)), POS), (dict(dq=P), ALIAS),
+])
+def test_bwd_ws_rejects_bad_arguments(kw, code):
+    assert _bwd_ws(**kw) == code
+
+
+def test_bwd_ws_empty_query_is_a_noop():
+    assert _bwd_ws(Sq=0, qseg=(0, 0), q=0, ws=0, ws_bytes=0) == OK
