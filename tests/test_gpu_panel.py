@@ -181,11 +181,13 @@ def test_panel_fullsize_t():
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
-def test_panel_fullsize_c3_head_groups():
-    """One rank's share of the 512K-token ring with a workspace for 5 of the 32 heads (7 head groups per ring
-    step): sampled rows and tail keys against the oracle, and the any-size properties."""
+@pytest.mark.parametrize("key", ["c3", "c4"])
+def test_panel_fullsize_ring_head_groups(key):
+    """One rank's share of the 512K-token ring, or of the 700K-token ring (43750-token chunks: ragged tiles and
+    panel blocks), with a workspace for 5 of the 32 heads (7 head groups per ring step): sampled rows and tail
+    keys against the oracle, and the any-size properties."""
     from tests.test_gpu_fullsize import _check_properties, _check_rows, _check_tail_keys
-    cfg = synth.get("c3")
+    cfg = synth.get(key)
     banner(f"panel {cfg.name}, head groups of 5")
     t = synth.make_ring_case(cfg, DEV)
     C = cfg.C
