@@ -18,6 +18,11 @@
 //             dP^T with the query on the lane axis and accumulates
 //             dQ^T += K^T dS^T in registers (K^T by transpose read of the
 //             row-major K tile).
+//  3'. dqs:   (ea_attn_bwd_ws) in place of 3: the dkdv pass also writes the
+//             bf16 dS it forms into a workspace panel (ea_device.h), and this
+//             pass computes dQ^T += K^T dS^T from it, one contraction per pair
+//             instead of three (bound by HBM bandwidth instead of the matrix
+//             cores).
 // All LDS tiles are row-major with the XOR chunk swizzle of ea_device.h.
 // The dq pass recomputes the two score products instead of exchanging dS
 // through atomics (fp32 atomic adds into L2 were measured at about 1.4 TB/s on
