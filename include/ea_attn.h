@@ -151,8 +151,9 @@ int ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, int 
  * back, in place of recomputing the scores and dP of every allowed pair.  The
  * panel holds one 16 KiB block per (256-query block, 32-key group) with any
  * allowed pair; ea_attn_bwd_ws_bytes gives its size for one (batch, head).
- * Heads are processed in groups of floor(ws_bytes / that size) (all B*H at once
- * if they fit), each group's two passes before the next group's.
+ * If the workspace holds all B*H panels, both passes run once over all of
+ * them; otherwise batch by batch, in groups of up to floor(ws_bytes / that
+ * size) heads of one batch, each group's two passes before the next group's.
  * workspace: device memory, 16-byte aligned, overlapping no other argument,
  * owned by the caller, contents undefined on entry and on return; calls that
  * share a workspace must be ordered on one stream.  Returns EA_ERR_WORKSPACE if
