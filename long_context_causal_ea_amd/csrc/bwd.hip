@@ -735,16 +735,20 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
     }
     const bf16x8 sb0 = pack_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
     const bf16x8 sb1 = pack_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-    // dQ^T += K^T dS^T; K^T read transposed from the row-major K tile
+    // dQ^T += K^T dS^T; K^T read transposed from the row-major K tile, first 16 keys for every block, then
+    // the next 16 (the first products need only the first pack)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const u32x2 lo0 = ds_read_tr16(&KV[stage][tofs[0][db]]);
       const u32x2 hi0 = ds_read_tr16(&KV[stage][tofs[1][db]]);
+      const u32x4 a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
+      dqa[db] = mfma32(as_bf16x8(a0), sb0, dqa[db]);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
       const u32x2 lo1 = ds_read_tr16(&KV[stage][tofs[0][db] + 16 * D]);
       const u32x2 hi1 = ds_read_tr16(&KV[stage][tofs[1][db] + 16 * D]);
-      const u32x4 a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
       const u32x4 a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
-      dqa[db] = mfma32(as_bf16x8(a0), sb0, dqa[db]);
       dqa[db] = mfma32(as_bf16x8(a1), sb1, dqa[db]);
     }
   };

@@ -276,11 +276,12 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
       pb[2 * mb] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       pb[2 * mb + 1] = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
     }
-    // O^T += V^T P^T; V^T read transposed from the row-major V tile
+    // O^T += V^T P^T; V^T read transposed from the row-major V tile.  Key steps outermost, so the first
+    // products need only the first packs of P (each accumulator still adds the key steps in order)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int kk = 0; kk < 2 * NMB; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < 2 * NMB; ++kk) {
+      for (int db = 0; db < NDB; ++db) {
         const u32x2 lo = ds_read_tr16(&Vs[stage][vofs[0][db] + 16 * kk * D]);
         const u32x2 hi = ds_read_tr16(&Vs[stage][vofs[1][db] + 16 * kk * D]);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
