@@ -36,9 +36,11 @@ O = 0 and zero gradients.
 
 The forward is computed two-pass per row: the row maximum first, then the sum
 of exponentials and P V using that maximum.  Rows are processed in blocks only
-to bound memory (rows are independent); inside a block the keys that no row of
-the block may see are dropped before the products, which removes exact zeros
-from the sums and nothing else.
+to bound memory (rows are independent; a block holds at most ROW_BLOCK_ELEMS
+scores, or the ``block_elems`` a caller passes); inside a block the keys that
+no row of the block may see are dropped before the products, which removes
+exact zeros from the sums and nothing else.  Key gradients add up over the
+blocks.
 """
 import numpy as np
 
@@ -78,7 +80,10 @@ def allowed_sums(pos_q, pos_k, causal: bool, weights) -> np.ndarray:
     return csum[n]
 
 
-def _row_blocks(sq: int, sk: int, budget_elems: int = 1 << 24):
+ROW_BLOCK_ELEMS = 1 << 24   # scores held at once (128 MiB of fp64)
+
+
+def _row_blocks(sq: int, sk: int, budget_elems: int):
     rows = max(1, min(sq, budget_elems // max(1, sk)))
     for i0 in range(0, sq, rows):
         yield i0, min(sq, i0 + rows)
@@ -105,8 +110,10 @@ def _useful_keys(pos_q_blk, pos_k, causal):
     return np.nonzero(pos_k <= pos_q_blk.max())[0] if pos_q_blk.size else np.arange(0)
 
 
-def attn_fwd(q, k, v, pos_q, pos_k, causal: bool, scale: float):
-    """One head.  q [Sq, D], k/v [Sk, D] -> O [Sq, D] fp64, LSE [Sq] fp64."""
+def attn_fwd(q, k, v, pos_q, pos_k, causal: bool, scale: float, block_elems=None):
+    """One head.  q [Sq, D], k/v [Sk, D] -> O [Sq, D] fp64, LSE [Sq] fp64.
+
+    block_elems: scores per row block (default ROW_BLOCK_ELEMS); any value gives the same result."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     pos_q = np.asarray(pos_q, dtype=np.int64)
     pos_k = np.asarray(pos_k, dtype=np.int64)
@@ -114,7 +121,7 @@ def attn_fwd(q, k, v, pos_q, pos_k, causal: bool, scale: float):
     sk = k.shape[0]
     o = np.zeros((sq, v.shape[1]), dtype=np.float64)
     lse = np.full(sq, NEG_INF)
-    for i0, i1 in _row_blocks(sq, sk):
+    for i0, i1 in _row_blocks(sq, sk, ROW_BLOCK_ELEMS if block_elems is None else block_elems):
         cols = _useful_keys(pos_q[i0:i1], pos_k, causal)
         if cols.size == 0:
             continue
@@ -125,8 +132,10 @@ def attn_fwd(q, k, v, pos_q, pos_k, causal: bool, scale: float):
     return o, lse
 
 
-def attn_bwd(q, k, v, do, pos_q, pos_k, causal: bool, scale: float):
-    """One head.  Returns dict with o, lse, delta, dq, dk, dv (all fp64)."""
+def attn_bwd(q, k, v, do, pos_q, pos_k, causal: bool, scale: float, block_elems=None):
+    """One head.  Returns dict with o, lse, delta, dq, dk, dv (all fp64).
+
+    block_elems: scores per row block (default ROW_BLOCK_ELEMS); any value gives the same result."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     pos_q = np.asarray(pos_q, dtype=np.int64)
     pos_k = np.asarray(pos_k, dtype=np.int64)
@@ -138,7 +147,7 @@ def attn_bwd(q, k, v, do, pos_q, pos_k, causal: bool, scale: float):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for i0, i1 in _row_blocks(sq, sk):
+    for i0, i1 in _row_blocks(sq, sk, ROW_BLOCK_ELEMS if block_elems is None else block_elems):
         cols = _useful_keys(pos_q[i0:i1], pos_k, causal)
         if cols.size == 0:
             continue

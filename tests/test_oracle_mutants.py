@@ -16,6 +16,7 @@ from oracle import rope as R
 from oracle import xent as X
 from oracle import zigzag as Z
 from tests import test_oracle as T
+from tests import test_oracle_blocks as TB
 from tests import test_oracle_rope as TR
 from tests import test_oracle_xent as TX
 
@@ -33,6 +34,25 @@ MUTANTS = {
     "pv_transposed_v": ("o = p @ vc", "o = p @ vc[::-1]"),
     "sums_strict": ('side="right"', 'side="left"'),
     "sums_unsorted": ("csum[n]", "csum[np.minimum(n + 1, len(csum) - 1)]"),
+    # the row-block path of the full-size comparisons
+    "dk_assigned_per_block": ("dk[cols] += scale * (ds.T @ q[i0:i1])", "dk[cols] = scale * (ds.T @ q[i0:i1])"),
+    "dv_assigned_per_block": ("dv[cols] += p.T @ dob", "dv[cols] = p.T @ dob"),
+    "block_end_off_by_one": ("yield i0, min(sq, i0 + rows)", "yield i0, min(sq, i0 + rows - 1)"),
+    "blocks_stop_one_row_early": ("for i0 in range(0, sq, rows):", "for i0 in range(0, sq - 1, rows):"),
+    "useful_keys_from_block_min": ("pos_k <= pos_q_blk.max()", "pos_k <= pos_q_blk.min()"),
+    # the [B, S, H, D] head wrappers
+    "fwd_heads_key_head_swapped": ("attn_fwd(q[b, :, h], k[b, :, h], v[b, :, h], pos_q",
+                                   "attn_fwd(q[b, :, h], k[b, :, n], v[b, :, h], pos_q"),
+    "bwd_heads_value_head_swapped": ("attn_bwd(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h]",
+                                     "attn_bwd(q[b, :, h], k[b, :, h], v[b, :, n], do[b, :, h]"),
+    "bwd_heads_batch_slot": ("res[key][b, :, n] = val", "res[key][0, :, n] = val"),
+}
+
+# mistakes in the [B, S, H, D] wrapper of the rotary oracle
+RHMUTANTS = {
+    "rope_heads_key_head_swapped": ("attn_bwd_rope(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h]",
+                                    "attn_bwd_rope(q[b, :, h], k[b, :, n], v[b, :, h], do[b, :, h]"),
+    "rope_heads_output_slot": ("res[key][b, :, n] = r[key]", "res[key][b, :, h] = r[key]"),
 }
 
 ZMUTANTS = {
@@ -91,6 +111,10 @@ PINS = [
     T.test_zero_query_counts_and_means,
     lambda: T.test_split_merge_equals_unsplit("random", True),
     lambda: T.test_allowed_sums_match_mask(True),
+    TB.test_row_blocks_partition_the_rows,
+    lambda: TB.test_row_blocks_match_bruteforce(True, "zigzag", 3),
+    lambda: TB.test_row_blocks_match_bruteforce(True, "random", 1),
+    lambda: TB.test_head_wrappers_match_batched_torch(True, False, None),
 ]
 
 ZPINS = [
@@ -121,7 +145,8 @@ def _fails(pins):
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_attention_mutant_is_caught(name, monkeypatch):
     mod = _load_mutant(A, *MUTANTS[name])
-    for fn in ("allowed_mask", "allowed_sums", "attn_fwd", "attn_bwd", "lse_merge", "_block_fwd"):
+    for fn in ("allowed_mask", "allowed_sums", "attn_fwd", "attn_bwd", "lse_merge", "_block_fwd", "_row_blocks",
+               "_useful_keys", "attn_fwd_heads", "attn_bwd_heads"):
         monkeypatch.setattr(A, fn, getattr(mod, fn))
     with np.errstate(all="ignore"):
         assert _fails(PINS) >= 1, f"no pin caught mutant {name}"
@@ -149,5 +174,12 @@ def test_rope_mutant_is_caught(name, monkeypatch):
     assert _fails(RPINS) >= 1, f"no pin caught mutant {name}"
 
 
+@pytest.mark.parametrize("name", sorted(RHMUTANTS))
+def test_rope_heads_mutant_is_caught(name, monkeypatch):
+    mod = _load_mutant(R, *RHMUTANTS[name])
+    monkeypatch.setattr(R, "attn_bwd_rope_heads", mod.attn_bwd_rope_heads)
+    assert _fails([TB.test_rope_head_wrapper_matches_single_heads]) >= 1, f"no pin caught mutant {name}"
+
+
 def test_unmutated_oracle_passes_all_pins():
-    assert _fails(PINS + ZPINS + XPINS + RPINS) == 0
+    assert _fails(PINS + ZPINS + XPINS + RPINS + [TB.test_rope_head_wrapper_matches_single_heads]) == 0
