@@ -39,7 +39,10 @@
  *  Mask.  EA_MASK_FULL allows every (query, key) pair; EA_MASK_CAUSAL allows
  *    key j for query i iff pos_k(j) <= pos_q(i) (the diagonal is kept).
  *  Scale.  scale multiplies <q_i, k_j>; it must be finite and > 0.
- *  Sizes.  B, H >= 1; D in {64, 128}; S >= 0 and < 2^31.
+ *  Sizes.  B, H >= 1; D in {64, 128}; S >= 0 and < 2^31.  Each launch is one
+ *    grid dimension of at most 2^32 - 1 threads; shapes that would need more
+ *    are EA_ERR_SHAPE (attention: B*H*ceil(S/256)*512 threads for queries,
+ *    B*H*ceil(Sk/128)*512 for keys, B*H*Sq*D/8 for Delta and the merge).
  *  Alignment.  q, k, v, o, dout and o_part must be 16-byte aligned; fp32
  *    arrays 4-byte aligned.
  *  Ownership.  The caller owns every buffer (device memory, except the
@@ -73,8 +76,7 @@ enum ea_status {
   EA_ERR_POSITIONS = 4,    /* bad segment count, lengths, starts or positions >= 2^31 */
   EA_ERR_ALIGN = 5,        /* pointer misaligned */
   EA_ERR_ALIAS = 6,        /* an output overlaps an input */
-  EA_ERR_HIP = 7,          /* a HIP launch failed */
-  EA_ERR_WORKSPACE = 8     /* workspace smaller than one (batch, head) needs */
+  EA_ERR_HIP = 7           /* a HIP launch failed */
 };
 
 enum ea_mask { EA_MASK_FULL = 0, EA_MASK_CAUSAL = 1 };
@@ -143,43 +145,55 @@ int ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, int 
                 int mask_mode, float scale, void* stream);
 
 /*
- * The same backward (same arguments, results and errors) with dS kept in a
- * caller-provided device workspace instead of recomputed.  The key-major pass
- * forms dS = P (dP - Delta) for each key block anyway; here it also writes it,
- * rounded to bf16 (the value the dk product uses), into the workspace, and the
- * dq pass becomes one contraction dq_i += scale * sum_j dS_ij k_j that reads it
- * back, in place of recomputing the scores and dP of every allowed pair.  The
- * panel holds one 16 KiB block per (256-query block, 32-key group) with any
- * allowed pair; ea_attn_bwd_ws_bytes gives its size for one (batch, head).
- * If the workspace holds all B*H panels, both passes run once over all of
- * them; otherwise batch by batch, in groups of up to floor(ws_bytes / that
- * size) heads of one batch, each group's two passes before the next group's.
- * workspace: device memory, 16-byte aligned, overlapping no other argument,
- * owned by the caller, contents undefined on entry and on return; calls that
- * share a workspace must be ordered on one stream.  Returns EA_ERR_WORKSPACE if
- * ws_bytes is below the size of one (batch, head), EA_ERR_NULL for a NULL
- * workspace when one is needed, otherwise as ea_attn_bwd.
+ * Forward and backward with the rotary position embedding fused in (the
+ * rotary base that the pages raise for long contexts: hotelren.com page,
+ * further optimisations; kwkr.cn ZeRO-3 offload page, training script
+ * rope-theta and advanced optimisation item 2; cn486.com page, training
+ * strategy).  The rotation is the one ea_rope applies (declared below): dims k
+ * and k + D/2 of a row at position p turn by p * theta^(-2k/D), fp64 angles,
+ * fp32 arithmetic, one rounding to bf16.  0 < theta finite, else
+ * EA_ERR_UNSUPPORTED.
+ *
+ * ea_attn_fwd_rope: q is the UNROTATED query [B,Sq,H,D] bf16; each row is
+ * turned by the angles of its position (from q_seg) in registers, right after
+ * it is loaded, and the turned rows are used for the scores.  k must already
+ * be rotated by its own positions (ea_rope with k_seg).  q_rot (optional, NULL
+ * for none): [B,Sq,H,D] bf16 with q's layout and q_batch_rows, 16-byte aligned,
+ * overlapping no other argument; receives the turned query rows, bit for bit
+ * what ea_rope would write, for the backward.  merge = 0 writes o (o_dtype) and
+ * lse like ea_attn_fwd; merge = 1 merges into the fp32 accumulator (o, lse) like
+ * ea_attn_fwd_merge (o_dtype must then be EA_F32).  Other arguments, results
+ * and errors as for those calls.
  */
-int ea_attn_bwd_ws(const void* q, const void* k, const void* v, const void* o, int o_dtype,
-                   const void* dout, const float* lse, float* delta, int delta_ready,
-                   float* dq, float* dk, float* dv,
-                   int B, int H, int64_t Sq, int64_t Sk, int D,
-                   int64_t q_batch_rows, int64_t k_batch_rows,
-                   const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg,
-                   int mask_mode, float scale, void* workspace, int64_t ws_bytes, void* stream);
+int ea_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, void* q_rot,
+                     int merge, int B, int H, int64_t Sq, int64_t Sk, int D,
+                     int64_t q_batch_rows, int64_t k_batch_rows,
+                     const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg,
+                     int mask_mode, float scale, double theta, void* stream);
 
 /*
- * Bytes of dS panel one (batch, head) of ea_attn_bwd_ws needs for these
- * segments and mask (host only; no HIP call).  Writes *bytes_per_head and
- * returns EA_OK, or EA_ERR_NULL / EA_ERR_POSITIONS / EA_ERR_UNSUPPORTED /
- * EA_ERR_SHAPE (a panel of 2^31 blocks or more) for bad arguments.
+ * ea_attn_bwd_rope: the backward of attention over rotated rows, returning the
+ * gradients with respect to the UNROTATED q and k.  q and k are the ROTATED
+ * rows the forward used (q_rot of ea_attn_fwd_rope, k rotated by ea_rope).
+ * The call computes dQ and dK of the rotated rows exactly as ea_attn_bwd does,
+ * then turns each row's contribution back by minus its angle (queries by
+ * q_seg, keys by k_seg) before adding it into dq and dk; dv and delta are as
+ * for ea_attn_bwd.  The rotation is linear, so contributions accumulated over
+ * several calls (a ring's steps) sum to the gradient of the unrotated inputs.
+ * Other arguments, results and errors as for ea_attn_bwd.
  */
-int ea_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, const int64_t* q_seg, int n_qseg, const int64_t* k_seg,
-                         int n_kseg, int mask_mode, int64_t* bytes_per_head);
+int ea_attn_bwd_rope(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                     const void* dout, const float* lse, float* delta, int delta_ready,
+                     float* dq, float* dk, float* dv,
+                     int B, int H, int64_t Sq, int64_t Sk, int D,
+                     int64_t q_batch_rows, int64_t k_batch_rows,
+                     const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg,
+                     int mask_mode, float scale, double theta, void* stream);
 
 /*
  * In-place LSE merge of a partial result over a disjoint key set into an
- * accumulator (ring attention combines one step's partial per rank visited):
+ * accumulator (ring attention combines one step's partial per rank visited;
+ * hotelren.com page, section 1 "sequence parallelism"):
  *   L   = ln(exp(lse_acc) + exp(lse_part))
  *   o_acc = exp(lse_acc - L) * o_acc + exp(lse_part - L) * o_part,  lse_acc = L.
  * A side whose LSE is -inf contributes nothing; both -inf gives (0, -inf).
@@ -207,8 +221,8 @@ int ea_lse_merge(float* o_acc, float* lse_acc, const void* o_part, int part_dtyp
  * mean over the rows that are not ignored pass grad_scale = 1 / that count.
  * Alignment: logits to their element size (any row_stride; rows that start
  * on 16 bytes are read and written in 16-byte pieces only), labels 8, loss and
- * lse 4.  Sizes: 0 <= rows < 2^31, 1 <= vocab <= row_stride,
- * vocab < 2^31.  loss, lse and labels must not overlap the logits or each
+ * lse 4.  Sizes: 0 <= rows < 2^23 (one 512-thread workgroup per row),
+ * 1 <= vocab <= row_stride, vocab < 2^31.  loss, lse and labels must not overlap the logits or each
  * other.  rows == 0 does nothing.  Enqueued on `stream` like the calls above.
  */
 int ea_xent_fwd_bwd(void* logits, int dtype, const int64_t* labels, float* loss, float* lse, int64_t rows,
@@ -229,8 +243,8 @@ int ea_xent_fwd_bwd(void* logits, int dtype, const int64_t* labels, float* loss,
  * for positions up to 2^31), the rotation in fp32, one rounding to the output.
  * x and y: dtype EA_BF16 or EA_F32 (both), same layout and batch stride
  * batch_rows * H * D elements, 16-byte aligned; y == x rotates in place,
- * otherwise they must not overlap.  D in {64, 128}; 0 < theta finite.
- * S == 0 does nothing.  Enqueued on `stream` like the calls above.
+ * otherwise they must not overlap.  D in {64, 128}; 0 < theta finite;
+ * B * S < 2^26 (64 threads per token row).  S == 0 does nothing.  Enqueued on `stream` like the calls above.
  */
 int ea_rope(const void* x, void* y, int dtype, int B, int H, int64_t S, int D, int64_t batch_rows,
             const int64_t* seg, int n_seg, double theta, int inverse, void* stream);
@@ -272,8 +286,7 @@ enum ea_kernel {
   EA_KERNEL_LSE_MERGE = 4,
   EA_KERNEL_XENT = 5,
   EA_KERNEL_ROPE = 6,
-  EA_KERNEL_BWD_DQ_PANEL = 7,  /* dq from the dS panel (ea_attn_bwd_ws) */
-  EA_KERNEL_COUNT = 8
+  EA_KERNEL_COUNT = 7
 };
 int ea_profile_begin(void);
 int ea_profile_end(void);

@@ -37,7 +37,7 @@ def lib():
         raise RuntimeError(
             f"HIP library not found at {LIB_PATH}; build it with `python -m long_context_causal_ea_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
-    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    vp, i32, i64, f32, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double
     pi64 = ctypes.POINTER(ctypes.c_int64)
     L.ea_attn_fwd.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i64, i64, i32, i64, i64,
                               pi64, i32, pi64, i32, i32, f32, vp]
@@ -45,19 +45,20 @@ def lib():
     L.ea_attn_fwd_merge.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i32, i64, i64,
                                     pi64, i32, pi64, i32, i32, f32, vp]
     L.ea_attn_fwd_merge.restype = i32
+    L.ea_attn_fwd_rope.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i64, i64, i32, i64, i64,
+                                   pi64, i32, pi64, i32, i32, f32, f64, vp]
+    L.ea_attn_fwd_rope.restype = i32
     L.ea_attn_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, i32, i32, i64, i64, i32,
                               i64, i64, pi64, i32, pi64, i32, i32, f32, vp]
     L.ea_attn_bwd.restype = i32
-    L.ea_attn_bwd_ws.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, i32, i32, i64, i64, i32,
-                                 i64, i64, pi64, i32, pi64, i32, i32, f32, vp, i64, vp]
-    L.ea_attn_bwd_ws.restype = i32
-    L.ea_attn_bwd_ws_bytes.argtypes = [i64, i64, pi64, i32, pi64, i32, i32, pi64]
-    L.ea_attn_bwd_ws_bytes.restype = i32
+    L.ea_attn_bwd_rope.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, i32, i32, i64, i64, i32,
+                                   i64, i64, pi64, i32, pi64, i32, i32, f32, f64, vp]
+    L.ea_attn_bwd_rope.restype = i32
     L.ea_lse_merge.argtypes = [vp, vp, vp, i32, vp, i32, i32, i64, i32, i64, vp]
     L.ea_lse_merge.restype = i32
     L.ea_xent_fwd_bwd.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, i64, f32, vp]
     L.ea_xent_fwd_bwd.restype = i32
-    L.ea_rope.argtypes = [vp, vp, i32, i32, i32, i64, i32, i64, pi64, i32, ctypes.c_double, i32, vp]
+    L.ea_rope.argtypes = [vp, vp, i32, i32, i32, i64, i32, i64, pi64, i32, f64, i32, vp]
     L.ea_rope.restype = i32
     L.ea_zigzag_segments.argtypes = [i64, i32, i32, pi64]
     L.ea_zigzag_segments.restype = i32
@@ -81,12 +82,12 @@ def lib():
     return L
 
 
-EXPORTS = ("ea_attn_fwd", "ea_attn_fwd_merge", "ea_attn_bwd", "ea_attn_bwd_ws", "ea_attn_bwd_ws_bytes", "ea_lse_merge", "ea_xent_fwd_bwd", "ea_rope", "ea_zigzag_segments",
-           "ea_ring_source",
+EXPORTS = ("ea_attn_fwd", "ea_attn_fwd_merge", "ea_attn_fwd_rope", "ea_attn_bwd", "ea_attn_bwd_rope",
+           "ea_lse_merge", "ea_xent_fwd_bwd", "ea_rope", "ea_zigzag_segments", "ea_ring_source",
            "ea_strerror", "ea_last_hip_error", "ea_version", "ea_profile_begin", "ea_profile_end",
            "ea_profile_query", "ea_kernel_name")
 
-KERNELS = ("fwd", "bwd_delta", "bwd_dkdv", "bwd_dq", "lse_merge", "xent", "rope", "bwd_dq_panel")
+KERNELS = ("fwd", "bwd_delta", "bwd_dkdv", "bwd_dq", "lse_merge", "xent", "rope")
 
 
 def strerror(status: int) -> str:
@@ -150,21 +151,68 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _require_bf16(*ts):
+def _dtype_is(name, t, *dtypes):
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+
+
+def _on_device(ref, tensors):
+    """Every tensor must live on ref's GPU (the kernels dereference these pointers on the device)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda" or t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}; every tensor of the call must be on one CUDA device "
+                             f"({ref.device if ref.device.type == 'cuda' else 'a CUDA device'})")
+
+
+def _attn_layout(q, k, q_side, k_side, stats):
+    """Shapes and row strides of one attention call, checked before anything reaches the library.
+
+    q [B, Sq, H, D] and k [B, Sk, H, D]; every tensor in q_side must have q's shape and batch row stride, every
+    one in k_side k's, every one in stats the shape [B, Sq, H] with q's batch row stride.  Returns
+    (B, Sq, H, D, Sk, q_batch_rows, k_batch_rows)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, S, H, D]")
+    B, sq, H, D = q.shape
+    sk = k.shape[1]
+    if tuple(k.shape) != (B, sk, H, D):
+        raise ValueError(f"k must be [B={B}, Sk, H={H}, D={D}], got {tuple(k.shape)}")
+    qbr, kbr = _rows(q, H, D), _rows(k, H, D)
+    for side, shape, br in ((q_side, (B, sq, H, D), qbr), (k_side, (B, sk, H, D), kbr)):
+        for name, t in side.items():
+            if t is None:
+                continue
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+            if _rows(t, H, D) != br:
+                raise ValueError(f"{name} must have the batch row stride of {'q' if br is qbr else 'k'}")
+    for name, t in stats.items():
+        if tuple(t.shape) != (B, sq, H):
+            raise ValueError(f"{name} must have shape {(B, sq, H)}, got {tuple(t.shape)}")
+        if _stat_rows(t, H) != qbr:
+            raise ValueError(f"{name} must have the batch row stride of q")
+    return B, sq, H, D, sk, qbr, kbr
+
+
+def _fwd_checks(q, k, v, o, lse, o_dtypes, q_rot=None):
     import torch
-    for t in ts:
-        if t is not None and t.dtype != torch.bfloat16:
-            raise ValueError("q, k, v and dout must be bfloat16")
+    bf = torch.bfloat16
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dtype_is(name, t, bf)
+    _dtype_is("o", o, *o_dtypes)
+    _dtype_is("lse", lse, torch.float32)
+    if q_rot is not None:
+        _dtype_is("q_rot", q_rot, bf)
+    dims = _attn_layout(q, k, {"o": o, "q_rot": q_rot}, {"v": v}, {"lse": lse})
+    _on_device(q, {"q": q, "k": k, "v": v, "o": o, "lse": lse, "q_rot": q_rot})
+    return dims
 
 
 def ea_attn_fwd(q, k, v, o, lse, q_seg, k_seg, causal=True, scale=None, stream=None):
-    """O and LSE of q against k/v.  Shapes [B,Sq,H,D], [B,Sk,H,D]; o [B,Sq,H,D]; lse [B,Sq,H]."""
-    _require_bf16(q, k, v)
-    B, sq, H, D = q.shape
-    sk = k.shape[1]
-    qbr, kbr = _rows(q, H, D), _rows(k, H, D)
-    if _rows(v, H, D) != kbr or _rows(o, H, D) != qbr or _stat_rows(lse, H) != qbr or v.shape[1] != sk:
-        raise ValueError("q/o/lse and k/v must share shapes and batch row strides")
+    """O and LSE of q against k/v.  Shapes [B,Sq,H,D], [B,Sk,H,D]; o [B,Sq,H,D] (fp32 or bf16); lse [B,Sq,H] fp32."""
+    import torch
+    B, sq, H, D, sk, qbr, kbr = _fwd_checks(q, k, v, o, lse, (torch.float32, torch.bfloat16))
     scale = D ** -0.5 if scale is None else float(scale)
     qs, nq = _segs(q_seg)
     ks, nk = _segs(k_seg)
@@ -177,14 +225,7 @@ def ea_attn_fwd(q, k, v, o, lse, q_seg, k_seg, causal=True, scale=None, stream=N
 def ea_attn_fwd_merge(q, k, v, o_acc, lse_acc, q_seg, k_seg, causal=True, scale=None, stream=None):
     """Forward of q against k/v merged in place into the fp32 accumulator (o_acc [B,Sq,H,D], lse_acc [B,Sq,H])."""
     import torch
-    _require_bf16(q, k, v)
-    if o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32:
-        raise TypeError("o_acc and lse_acc must be float32")
-    B, sq, H, D = q.shape
-    sk = k.shape[1]
-    qbr, kbr = _rows(q, H, D), _rows(k, H, D)
-    if _rows(v, H, D) != kbr or _rows(o_acc, H, D) != qbr or _stat_rows(lse_acc, H) != qbr or v.shape[1] != sk:
-        raise ValueError("q/o_acc/lse_acc and k/v must share shapes and batch row strides")
+    B, sq, H, D, sk, qbr, kbr = _fwd_checks(q, k, v, o_acc, lse_acc, (torch.float32,))
     scale = D ** -0.5 if scale is None else float(scale)
     qs, nq = _segs(q_seg)
     ks, nk = _segs(k_seg)
@@ -194,56 +235,77 @@ def ea_attn_fwd_merge(q, k, v, o_acc, lse_acc, q_seg, k_seg, causal=True, scale=
     _check(st, "ea_attn_fwd_merge")
 
 
-def ea_attn_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, q_seg, k_seg, causal=True, scale=None,
-                delta_ready=False, stream=None, workspace=None):
-    """Accumulates dq, dk, dv (fp32) for the final (o, lse); writes delta unless delta_ready.
+def ea_attn_fwd_rope(q, k, v, o, lse, q_seg, k_seg, theta, q_rot=None, merge=False, causal=True, scale=None,
+                     stream=None):
+    """Forward with q UNROTATED (turned by its positions in the kernel) and k already rotated (ea_rope).
 
-    workspace: None recomputes the scores for dq (``ea_attn_bwd``); a device tensor (any dtype, contiguous)
-    keeps the bf16 dS panel there and computes dq from it (``ea_attn_bwd_ws``; size per (batch, head) from
-    ``ea_attn_bwd_ws_bytes``)."""
-    _require_bf16(q, k, v, dout)
-    B, sq, H, D = q.shape
-    sk = k.shape[1]
-    qbr, kbr = _rows(q, H, D), _rows(k, H, D)
-    for t, r in ((dout, qbr), (dq, qbr), (v, kbr), (dk, kbr), (dv, kbr)):
-        if _rows(t, H, D) != r:
-            raise ValueError("inconsistent batch row strides")
-    if o is not None and _rows(o, H, D) != qbr:
-        raise ValueError("inconsistent batch row strides")
-    if _stat_rows(lse, H) != qbr or _stat_rows(delta, H) != qbr:
-        raise ValueError("inconsistent statistics row strides")
+    q_rot: optional bf16 [B,Sq,H,D] that receives the turned q for the backward.  merge=True merges into the fp32
+    accumulator (o, lse) like ea_attn_fwd_merge; otherwise o (fp32 or bf16) and lse are written."""
+    import torch
+    dts = (torch.float32,) if merge else (torch.float32, torch.bfloat16)
+    B, sq, H, D, sk, qbr, kbr = _fwd_checks(q, k, v, o, lse, dts, q_rot)
     scale = D ** -0.5 if scale is None else float(scale)
     qs, nq = _segs(q_seg)
     ks, nk = _segs(k_seg)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o) if o is not None else EA_F32,
+    st = lib().ea_attn_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(q_rot),
+                                1 if merge else 0, B, H, sq, sk, D, qbr, kbr, qs, nq, ks, nk,
+                                EA_MASK_CAUSAL if causal else EA_MASK_FULL, scale, float(theta), _stream(stream))
+    _check(st, "ea_attn_fwd_rope")
+
+
+def _bwd_args(q, k, v, o, dout, lse, delta, dq, dk, dv, q_seg, k_seg, causal, scale, delta_ready):
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _dtype_is(name, t, bf)
+    if o is not None:
+        _dtype_is("o", o, f32, bf)
+    elif not delta_ready:
+        raise ValueError("o is needed unless delta_ready")
+    for name, t in (("lse", lse), ("delta", delta), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _dtype_is(name, t, f32)
+    B, sq, H, D, sk, qbr, kbr = _attn_layout(q, k, {"o": o, "dout": dout, "dq": dq}, {"v": v, "dk": dk, "dv": dv},
+                                             {"lse": lse, "delta": delta})
+    _on_device(q, {"q": q, "k": k, "v": v, "o": o, "dout": dout, "lse": lse, "delta": delta, "dq": dq, "dk": dk,
+                   "dv": dv})
+    scale = D ** -0.5 if scale is None else float(scale)
+    qs, nq = _segs(q_seg)
+    ks, nk = _segs(k_seg)
+    return (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o) if o is not None else EA_F32,
             _ptr(dout), _ptr(lse), _ptr(delta), 1 if delta_ready else 0, _ptr(dq), _ptr(dk),
             _ptr(dv), B, H, sq, sk, D, qbr, kbr, qs, nq, ks, nk,
             EA_MASK_CAUSAL if causal else EA_MASK_FULL, scale)
-    if workspace is None:
-        _check(lib().ea_attn_bwd(*args, _stream(stream)), "ea_attn_bwd")
-        return
-    if not workspace.is_contiguous():
-        raise ValueError("workspace must be contiguous")
-    nbytes = workspace.numel() * workspace.element_size()
-    _check(lib().ea_attn_bwd_ws(*args, _ptr(workspace), nbytes, _stream(stream)), "ea_attn_bwd_ws")
 
 
-def ea_attn_bwd_ws_bytes(sq: int, sk: int, q_seg, k_seg, causal=True) -> int:
-    """Bytes of dS panel one (batch, head) of ``ea_attn_bwd_ws`` needs."""
-    qs, nq = _segs(q_seg)
-    ks, nk = _segs(k_seg)
-    out = ctypes.c_int64(0)
-    st = lib().ea_attn_bwd_ws_bytes(int(sq), int(sk), qs, nq, ks, nk, EA_MASK_CAUSAL if causal else EA_MASK_FULL,
-                                    ctypes.byref(out))
-    _check(st, "ea_attn_bwd_ws_bytes")
-    return int(out.value)
+def ea_attn_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, q_seg, k_seg, causal=True, scale=None,
+                delta_ready=False, stream=None):
+    """Accumulates dq, dk, dv (fp32) for the final (o, lse); writes delta unless delta_ready."""
+    args = _bwd_args(q, k, v, o, dout, lse, delta, dq, dk, dv, q_seg, k_seg, causal, scale, delta_ready)
+    _check(lib().ea_attn_bwd(*args, _stream(stream)), "ea_attn_bwd")
+
+
+def ea_attn_bwd_rope(q, k, v, o, dout, lse, delta, dq, dk, dv, q_seg, k_seg, theta, causal=True, scale=None,
+                     delta_ready=False, stream=None):
+    """ea_attn_bwd on ROTATED q, k (q_rot of ea_attn_fwd_rope, k from ea_rope); dq and dk accumulate the
+    gradients with respect to the unrotated rows."""
+    args = _bwd_args(q, k, v, o, dout, lse, delta, dq, dk, dv, q_seg, k_seg, causal, scale, delta_ready)
+    _check(lib().ea_attn_bwd_rope(*args, float(theta), _stream(stream)), "ea_attn_bwd_rope")
 
 
 def ea_lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
+    """In place: (o_acc, lse_acc) <- merge with (o_part, lse_part).  o_acc fp32 [B,Sq,H,D], o_part fp32 or bf16
+    of the same shape, lse_acc and lse_part fp32 [B,Sq,H]."""
+    import torch
+    _dtype_is("o_acc", o_acc, torch.float32)
+    _dtype_is("o_part", o_part, torch.float32, torch.bfloat16)
+    _dtype_is("lse_acc", lse_acc, torch.float32)
+    _dtype_is("lse_part", lse_part, torch.float32)
+    if o_acc.dim() != 4:
+        raise ValueError("o_acc must be [B, S, H, D]")
     B, sq, H, D = o_acc.shape
+    _attn_layout(o_acc, o_acc, {"o_part": o_part}, {}, {"lse_acc": lse_acc, "lse_part": lse_part})
+    _on_device(o_acc, {"o_acc": o_acc, "lse_acc": lse_acc, "o_part": o_part, "lse_part": lse_part})
     qbr = _rows(o_acc, H, D)
-    if _rows(o_part, H, D) != qbr or _stat_rows(lse_acc, H) != qbr or _stat_rows(lse_part, H) != qbr:
-        raise ValueError("inconsistent batch row strides")
     st = lib().ea_lse_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _dtype_code(o_part), _ptr(lse_part),
                             B, H, sq, D, qbr, _stream(stream))
     _check(st, "ea_lse_merge")
@@ -257,9 +319,11 @@ def ea_xent_fwd_bwd(logits, labels, loss, lse, grad_scale=1.0, ignore_index=-100
         raise ValueError("logits must be [rows, vocab] with contiguous rows")
     rows, vocab = logits.shape
     row_stride = logits.stride(0) if rows > 1 else vocab
+    _dtype_is("logits", logits, torch.float32, torch.bfloat16)
     for t, dt, name in ((labels, torch.int64, "labels"), (loss, torch.float32, "loss"), (lse, torch.float32, "lse")):
         if t.dtype != dt or t.dim() != 1 or t.shape[0] != rows or (rows > 1 and t.stride(0) != 1):
             raise ValueError(f"{name} must be a contiguous {dt} vector of {rows} rows")
+    _on_device(logits, {"logits": logits, "labels": labels, "loss": loss, "lse": lse})
     st = lib().ea_xent_fwd_bwd(_ptr(logits), _dtype_code(logits), _ptr(labels), _ptr(loss), _ptr(lse), rows,
                                vocab, row_stride, int(ignore_index), float(grad_scale), _stream(stream))
     _check(st, "ea_xent_fwd_bwd")
@@ -268,12 +332,15 @@ def ea_xent_fwd_bwd(logits, labels, loss, lse, grad_scale=1.0, ignore_index=-100
 def ea_rope(x, y, seg, theta, inverse=False, stream=None):
     """Rotary embedding of x [B, S, H, D] (bf16 or fp32) by the positions of seg into y (same shape, dtype and
     batch stride; y may be x).  inverse=True applies the transpose (for gradients)."""
+    import torch
     if x.dim() != 4 or y.shape != x.shape or y.dtype != x.dtype:
         raise ValueError("x and y must be [B, S, H, D] tensors of one shape and dtype")
+    _dtype_is("x", x, torch.float32, torch.bfloat16)
     B, S, H, D = x.shape
     rows = _rows(x, H, D)
     if _rows(y, H, D) != rows:
         raise ValueError("x and y must have the same batch stride")
+    _on_device(x, {"x": x, "y": y})
     sg, ns = _segs(seg)
     st = lib().ea_rope(_ptr(x), _ptr(y), _dtype_code(x), B, H, S, D, rows, sg, ns, float(theta), int(bool(inverse)),
                        _stream(stream))

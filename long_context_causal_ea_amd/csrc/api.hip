@@ -101,6 +101,13 @@ bool overlap(const Span& a, const Span& b) {
   return a.lo < b.hi && b.lo < a.hi;
 }
 
+// A HIP launch takes at most 2^32 - 1 threads in one grid dimension; every
+// launcher here uses one dimension.  Rounded up to whole workgroups.
+bool grid_fits(int64_t threads, int64_t block) {
+  const int64_t wgs = (threads + block - 1) / block;
+  return wgs * block <= (((int64_t)1 << 32) - 1);
+}
+
 int check_common(int B, int H, int64_t Sq, int64_t Sk, int D, int64_t qbr, int64_t kbr, int mask_mode,
                  float scale) {
   if (B < 1 || H < 1 || Sq < 0 || Sk < 0 || Sq >= kPosLimit || Sk >= kPosLimit) return EA_ERR_SHAPE;
@@ -109,19 +116,26 @@ int check_common(int B, int H, int64_t Sq, int64_t Sk, int D, int64_t qbr, int64
   if (D != 64 && D != 128) return EA_ERR_UNSUPPORTED;
   if (mask_mode != EA_MASK_FULL && mask_mode != EA_MASK_CAUSAL) return EA_ERR_UNSUPPORTED;
   if (!(scale > 0.f) || !isfinite(scale)) return EA_ERR_UNSUPPORTED;
-  // grid sizes: one workgroup per 128 rows per (batch, head)
-  const int64_t blocks_q = (Sq + 127) / 128, blocks_k = (Sk + 127) / 128;
+  // grids: forward and dq one 512-thread workgroup per 256 query rows per (batch, head), dk/dv one per 128
+  // keys, Delta D/8 threads per (row, head)
   const int64_t bh = (int64_t)B * H;
-  if (bh * blocks_q >= kPosLimit || bh * blocks_k >= kPosLimit) return EA_ERR_SHAPE;
-  if (bh * Sq * (D / 8) >= ((int64_t)1 << 40)) return EA_ERR_SHAPE;
+  if (!grid_fits(bh * ((Sq + 255) / 256) * 512, 512) || !grid_fits(bh * ((Sk + 127) / 128) * 512, 512))
+    return EA_ERR_SHAPE;
+  if (!grid_fits(bh * Sq * (D / 8), 256)) return EA_ERR_SHAPE;
   return EA_OK;
+}
+
+bool theta_ok(double theta) { return theta > 0.0 && isfinite(theta); }
+
+void rope_freqs(double theta, int D, double* f) {
+  for (int k = 0; k < 64; ++k) f[k] = k < D / 2 ? pow(theta, -2.0 * k / D) : 0.0;
 }
 
 }  // namespace
 
 extern "C" {
 
-int ea_version(void) { return 100; }  // 0.1.0
+int ea_version(void) { return 200; }  // 0.2.0
 
 const char* ea_strerror(int status) {
   switch (status) {
@@ -133,7 +147,6 @@ const char* ea_strerror(int status) {
     case EA_ERR_ALIGN: return "pointer misaligned (the alignment each call documents in ea_attn.h)";
     case EA_ERR_ALIAS: return "an output buffer overlaps an input buffer";
     case EA_ERR_HIP: return "a HIP launch failed (see ea_last_hip_error)";
-    case EA_ERR_WORKSPACE: return "workspace smaller than one (batch, head) of the dS panel needs";
     default: return "unknown status";
   }
 }
@@ -187,7 +200,6 @@ const char* ea_kernel_name(int kernel) {
     case EA_KERNEL_LSE_MERGE: return "lse_merge";
     case EA_KERNEL_XENT: return "xent";
     case EA_KERNEL_ROPE: return "rope";
-    case EA_KERNEL_BWD_DQ_PANEL: return "bwd_dq_panel";
     default: return "unknown";
   }
 }
@@ -209,13 +221,18 @@ int ea_zigzag_segments(int64_t s_total, int world, int rank, int64_t* seg_out) {
   return EA_OK;
 }
 
+// rope: 0 none; 1 turn q by the rotary angles of its positions (theta), writing
+// the turned rows to q_rot when it is not NULL.
 static int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, int B, int H,
                     int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
                     int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, int merge,
-                    void* stream) {
+                    int rope, double theta, void* q_rot, void* stream) {
   int st = check_common(B, H, Sq, Sk, D, q_batch_rows, k_batch_rows, mask_mode, scale);
   if (st) return st;
   if (o_dtype != EA_F32 && o_dtype != EA_BF16) return EA_ERR_UNSUPPORTED;
+  if (merge != 0 && merge != 1) return EA_ERR_UNSUPPORTED;
+  if (merge && o_dtype != EA_F32) return EA_ERR_UNSUPPORTED;
+  if (rope && !theta_ok(theta)) return EA_ERR_UNSUPPORTED;
   ea::FwdArgs a;
   if ((st = check_segs(q_seg, n_qseg, Sq, &a.qs))) return st;
   if ((st = check_segs(k_seg, n_kseg, Sk, &a.ks))) return st;
@@ -233,6 +250,12 @@ static int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_
     for (const Span& in : {sq, sk, sv})
       if (overlap(out, in)) return EA_ERR_ALIAS;
   if (overlap(so, sl)) return EA_ERR_ALIAS;
+  if (rope && q_rot) {
+    if (!aligned(q_rot, 16)) return EA_ERR_ALIGN;
+    const Span sr = span_of(q_rot, B, q_batch_rows, Sq, row, 2);
+    for (const Span& x : {sq, sk, sv, so, sl})
+      if (overlap(sr, x)) return EA_ERR_ALIAS;
+  }
 
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -250,6 +273,9 @@ static int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_
   a.o_bf16 = o_dtype == EA_BF16;
   a.merge = merge;
   a.scale = scale;
+  a.rope = rope;
+  a.q_rot = rope ? static_cast<uint16_t*>(q_rot) : nullptr;
+  rope_freqs(rope ? theta : 1.0, D, a.inv_freq);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = timed_launch(EA_KERNEL_FWD, s, [&] { return ea::launch_fwd(a, s); });
   return e == hipSuccess ? EA_OK : hip_fail(e);
@@ -259,7 +285,7 @@ int ea_attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtyp
                 int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
                 int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, void* stream) {
   return attn_fwd(q, k, v, o, o_dtype, lse, B, H, Sq, Sk, D, q_batch_rows, k_batch_rows, q_seg, n_qseg, k_seg,
-                  n_kseg, mask_mode, scale, 0, stream);
+                  n_kseg, mask_mode, scale, 0, 0, 0.0, nullptr, stream);
 }
 
 int ea_attn_fwd_merge(const void* q, const void* k, const void* v, float* o_acc, float* lse_acc, int B, int H,
@@ -267,25 +293,32 @@ int ea_attn_fwd_merge(const void* q, const void* k, const void* v, float* o_acc,
                       const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode,
                       float scale, void* stream) {
   return attn_fwd(q, k, v, o_acc, EA_F32, lse_acc, B, H, Sq, Sk, D, q_batch_rows, k_batch_rows, q_seg, n_qseg,
-                  k_seg, n_kseg, mask_mode, scale, 1, stream);
+                  k_seg, n_kseg, mask_mode, scale, 1, 0, 0.0, nullptr, stream);
+}
+
+int ea_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, void* q_rot,
+                     int merge, int B, int H, int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows,
+                     int64_t k_batch_rows, const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg,
+                     int mask_mode, float scale, double theta, void* stream) {
+  return attn_fwd(q, k, v, o, o_dtype, lse, B, H, Sq, Sk, D, q_batch_rows, k_batch_rows, q_seg, n_qseg, k_seg,
+                  n_kseg, mask_mode, scale, merge, 1, theta, q_rot, stream);
 }
 
 }  // extern "C"
 
 namespace {
 
-constexpr int64_t kPanelBlockBytes = (int64_t)256 * 32 * 2;  // one (256-query, 32-key) bf16 block
-
-// use_ws == 0: dq by recomputation (ea_attn_bwd); 1: dq from the dS panel in
-// the workspace (ea_attn_bwd_ws).
+// rope: 0 none; 1 q and k are rows turned by their rotary angles (theta), and the
+// dq, dk contributions are turned back before they are added.
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dout,
              const float* lse, float* delta, int delta_ready, float* dq, float* dk, float* dv, int B, int H,
              int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
-             int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, int use_ws, void* ws,
-             int64_t ws_bytes, void* stream) {
+             int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, int rope, double theta,
+             void* stream) {
   int st = check_common(B, H, Sq, Sk, D, q_batch_rows, k_batch_rows, mask_mode, scale);
   if (st) return st;
   if (o_dtype != EA_F32 && o_dtype != EA_BF16) return EA_ERR_UNSUPPORTED;
+  if (rope && !theta_ok(theta)) return EA_ERR_UNSUPPORTED;
   ea::BwdArgs a;
   if ((st = check_segs(q_seg, n_qseg, Sq, &a.qs))) return st;
   if ((st = check_segs(k_seg, n_kseg, Sk, &a.ks))) return st;
@@ -312,19 +345,6 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_d
   if (overlap(sdq, sdk) || overlap(sdq, sdv) || overlap(sdk, sdv) || overlap(sdl, sdq) || overlap(sdl, sdk) ||
       overlap(sdl, sdv))
     return EA_ERR_ALIAS;
-  int64_t per_bh = 0;  // panel blocks per (batch, head)
-  if (use_ws && Sk > 0) {
-    per_bh = ea::panel_blocks(a.qs, a.ks, mask_mode == EA_MASK_CAUSAL);
-    if (per_bh >= kPosLimit) return EA_ERR_SHAPE;
-    if (per_bh > 0) {
-      if (!ws) return EA_ERR_NULL;
-      if (!aligned(ws, 16)) return EA_ERR_ALIGN;
-      if (ws_bytes < per_bh * kPanelBlockBytes) return EA_ERR_WORKSPACE;
-      const Span sw{(uintptr_t)ws, (uintptr_t)ws + (uintptr_t)ws_bytes};
-      for (const Span& x : {sq, sk, sv, sdo, sl, so, sdl, sdq, sdk, sdv})
-        if (overlap(sw, x)) return EA_ERR_ALIAS;
-    }
-  }
 
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -347,55 +367,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_d
   a.o_bf16 = o_dtype == EA_BF16;
   a.scale = scale;
   a.Hs = H;
-  a.ds = nullptr;
-  a.ds_per_bh = 0;
+  a.rope = rope;
+  rope_freqs(rope ? theta : 1.0, D, a.inv_freq);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (!delta_ready) e = timed_launch(EA_KERNEL_BWD_DELTA, s, [&] { return ea::launch_bwd_delta(a, s); });
   if (e != hipSuccess) return hip_fail(e);
   if (Sk == 0) return EA_OK;
-  if (!use_ws) {
-    e = timed_launch(EA_KERNEL_BWD_DKDV, s, [&] { return ea::launch_bwd_dkdv(a, s); });
-    if (e != hipSuccess) return hip_fail(e);
-    e = timed_launch(EA_KERNEL_BWD_DQ, s, [&] { return ea::launch_bwd_dq(a, s); });
-    return e == hipSuccess ? EA_OK : hip_fail(e);
-  }
-  if (per_bh == 0) return EA_OK;  // no allowed pair anywhere: nothing to accumulate
-  // groups of heads whose panels fit the workspace, each group's two passes in turn
-  const int64_t cap = ws_bytes / (per_bh * kPanelBlockBytes);
-  a.ds = static_cast<uint16_t*>(ws);
-  a.ds_per_bh = (int)per_bh;
-  auto run = [&](const ea::BwdArgs& g) {
-    hipError_t r = timed_launch(EA_KERNEL_BWD_DKDV, s, [&] { return ea::launch_bwd_dkdv(g, s); });
-    if (r != hipSuccess) return r;
-    return timed_launch(EA_KERNEL_BWD_DQ_PANEL, s, [&] { return ea::launch_bwd_dqs(g, s); });
-  };
-  if (cap >= (int64_t)B * H) {
-    e = run(a);
-    return e == hipSuccess ? EA_OK : hip_fail(e);
-  }
-  const int G = (int)(cap < H ? cap : H);
-  for (int b = 0; b < B; ++b)
-    for (int h0 = 0; h0 < H; h0 += G) {
-      ea::BwdArgs g = a;
-      const int64_t tok = (int64_t)b * q_batch_rows * H * D + (int64_t)h0 * D;
-      const int64_t ktok = (int64_t)b * k_batch_rows * H * D + (int64_t)h0 * D;
-      const int64_t row = (int64_t)b * q_batch_rows * H + h0;
-      g.B = 1;
-      g.H = H - h0 < G ? H - h0 : G;
-      g.q = a.q + tok;
-      g.dout = a.dout + tok;
-      g.dq = a.dq + tok;
-      g.k = a.k + ktok;
-      g.v = a.v + ktok;
-      g.dk = a.dk + ktok;
-      g.dv = a.dv + ktok;
-      g.lse = a.lse + row;
-      g.delta = a.delta + row;
-      e = run(g);
-      if (e != hipSuccess) return hip_fail(e);
-    }
-  return EA_OK;
+  e = timed_launch(EA_KERNEL_BWD_DKDV, s, [&] { return ea::launch_bwd_dkdv(a, s); });
+  if (e != hipSuccess) return hip_fail(e);
+  e = timed_launch(EA_KERNEL_BWD_DQ, s, [&] { return ea::launch_bwd_dq(a, s); });
+  return e == hipSuccess ? EA_OK : hip_fail(e);
 }
 
 }  // namespace
@@ -407,31 +389,16 @@ int ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, int 
                 int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
                 int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, void* stream) {
   return attn_bwd(q, k, v, o, o_dtype, dout, lse, delta, delta_ready, dq, dk, dv, B, H, Sq, Sk, D, q_batch_rows,
-                  k_batch_rows, q_seg, n_qseg, k_seg, n_kseg, mask_mode, scale, 0, nullptr, 0, stream);
+                  k_batch_rows, q_seg, n_qseg, k_seg, n_kseg, mask_mode, scale, 0, 0.0, stream);
 }
 
-int ea_attn_bwd_ws(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dout,
-                   const float* lse, float* delta, int delta_ready, float* dq, float* dk, float* dv, int B, int H,
-                   int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows, const int64_t* q_seg,
-                   int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale, void* workspace,
-                   int64_t ws_bytes, void* stream) {
+int ea_attn_bwd_rope(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dout,
+                     const float* lse, float* delta, int delta_ready, float* dq, float* dk, float* dv, int B, int H,
+                     int64_t Sq, int64_t Sk, int D, int64_t q_batch_rows, int64_t k_batch_rows,
+                     const int64_t* q_seg, int n_qseg, const int64_t* k_seg, int n_kseg, int mask_mode, float scale,
+                     double theta, void* stream) {
   return attn_bwd(q, k, v, o, o_dtype, dout, lse, delta, delta_ready, dq, dk, dv, B, H, Sq, Sk, D, q_batch_rows,
-                  k_batch_rows, q_seg, n_qseg, k_seg, n_kseg, mask_mode, scale, 1, workspace, ws_bytes, stream);
-}
-
-int ea_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, const int64_t* q_seg, int n_qseg, const int64_t* k_seg,
-                         int n_kseg, int mask_mode, int64_t* bytes_per_head) {
-  if (!bytes_per_head) return EA_ERR_NULL;
-  if (Sq < 0 || Sk < 0 || Sq >= kPosLimit || Sk >= kPosLimit) return EA_ERR_SHAPE;
-  if (mask_mode != EA_MASK_FULL && mask_mode != EA_MASK_CAUSAL) return EA_ERR_UNSUPPORTED;
-  SegArg qs, ks;
-  int st;
-  if ((st = check_segs(q_seg, n_qseg, Sq, &qs))) return st;
-  if ((st = check_segs(k_seg, n_kseg, Sk, &ks))) return st;
-  const int64_t n = (Sq == 0 || Sk == 0) ? 0 : ea::panel_blocks(qs, ks, mask_mode == EA_MASK_CAUSAL);
-  if (n >= kPosLimit) return EA_ERR_SHAPE;
-  *bytes_per_head = n * kPanelBlockBytes;
-  return EA_OK;
+                  k_batch_rows, q_seg, n_qseg, k_seg, n_kseg, mask_mode, scale, 1, theta, stream);
 }
 
 int ea_lse_merge(float* o_acc, float* lse_acc, const void* o_part, int part_dtype, const float* lse_part, int B,
@@ -440,7 +407,7 @@ int ea_lse_merge(float* o_acc, float* lse_acc, const void* o_part, int part_dtyp
     return EA_ERR_SHAPE;
   if (D != 64 && D != 128) return EA_ERR_UNSUPPORTED;
   if (part_dtype != EA_F32 && part_dtype != EA_BF16) return EA_ERR_UNSUPPORTED;
-  if ((int64_t)B * H * Sq * (D / 8) >= ((int64_t)1 << 40)) return EA_ERR_SHAPE;
+  if (!grid_fits((int64_t)B * H * Sq * (D / 8), 256)) return EA_ERR_SHAPE;
   if (Sq == 0) return EA_OK;
   if (!o_acc || !lse_acc || !o_part || !lse_part) return EA_ERR_NULL;
   if (!aligned(o_acc, 16) || !aligned(o_part, 16) || !aligned(lse_acc, 4) || !aligned(lse_part, 4))
@@ -470,6 +437,7 @@ int ea_lse_merge(float* o_acc, float* lse_acc, const void* o_part, int part_dtyp
 int ea_xent_fwd_bwd(void* logits, int dtype, const int64_t* labels, float* loss, float* lse, int64_t rows,
                     int64_t vocab, int64_t row_stride, int64_t ignore_index, float grad_scale, void* stream) {
   if (rows < 0 || rows >= kPosLimit || vocab < 1 || vocab >= kPosLimit || row_stride < vocab) return EA_ERR_SHAPE;
+  if (!grid_fits(rows * ea::kXentBlock, ea::kXentBlock)) return EA_ERR_SHAPE;  // one workgroup per row
   if (dtype != EA_F32 && dtype != EA_BF16) return EA_ERR_UNSUPPORTED;
   if (!isfinite(grad_scale)) return EA_ERR_UNSUPPORTED;
   if (rows == 0) return EA_OK;
@@ -503,9 +471,10 @@ int ea_rope(const void* x, void* y, int dtype, int B, int H, int64_t S, int D, i
             const int64_t* seg, int n_seg, double theta, int inverse, void* stream) {
   if (B < 1 || H < 1 || S < 0 || S >= kPosLimit || batch_rows < S || batch_rows >= kPosLimit) return EA_ERR_SHAPE;
   if ((int64_t)B * S >= kPosLimit) return EA_ERR_SHAPE;
+  if (!grid_fits((int64_t)B * S * (ea::kRopeBlock / ea::kRopeRowsPerBlock), ea::kRopeBlock)) return EA_ERR_SHAPE;
   if (D != 64 && D != 128) return EA_ERR_UNSUPPORTED;
   if (dtype != EA_F32 && dtype != EA_BF16) return EA_ERR_UNSUPPORTED;
-  if (!(theta > 0.0) || !isfinite(theta)) return EA_ERR_UNSUPPORTED;
+  if (!theta_ok(theta)) return EA_ERR_UNSUPPORTED;
   if (inverse != 0 && inverse != 1) return EA_ERR_UNSUPPORTED;
   ea::RopeArgs a;
   int st = check_segs(seg, n_seg, S, &a.seg);
@@ -525,7 +494,7 @@ int ea_rope(const void* x, void* y, int dtype, int B, int H, int64_t S, int D, i
   a.batch_rows = batch_rows;
   a.inverse = inverse;
   a.bf16 = dtype == EA_BF16;
-  for (int k = 0; k < 64; ++k) a.inv_freq[k] = k < D / 2 ? pow(theta, -2.0 * k / D) : 0.0;
+  rope_freqs(theta, D, a.inv_freq);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = timed_launch(EA_KERNEL_ROPE, s, [&] { return ea::launch_rope(a, s); });
   return e == hipSuccess ? EA_OK : hip_fail(e);

@@ -18,11 +18,6 @@
 //             dP^T with the query on the lane axis and accumulates
 //             dQ^T += K^T dS^T in registers (K^T by transpose read of the
 //             row-major K tile).
-//  3'. dqs:   (ea_attn_bwd_ws) in place of 3: the dkdv pass also writes the
-//             bf16 dS it forms into a workspace panel (ea_device.h), and this
-//             pass computes dQ^T += K^T dS^T from it, one contraction per pair
-//             instead of three (bound by HBM bandwidth instead of the matrix
-//             cores).
 // All LDS tiles are row-major with the XOR chunk swizzle of ea_device.h.
 // The dq pass recomputes the two score products instead of exchanging dS
 // through atomics (fp32 atomic adds into L2 were measured at about 1.4 TB/s on
@@ -50,11 +45,11 @@ struct BwdParams {
   long q_bstride, k_bstride, row_bstride;  // elements between batches (tokens*H*D, tokens*H*D, tokens*H)
   long rs;                                 // Hs*D
   int H, Hs, Sq, Sk, nblk;                 // heads in this launch, heads per token row
-  uint16_t* ds;                            // dS panel (bf16), or null
-  int ds_per_bh;                           // panel blocks per (batch, head)
   Seg qs, ks;
   int causal, o_bf16;
   float scale, c;
+  int rope;       // 1: q and k are rotated rows; dq and dk are turned back before they are added
+  double f[64];   // rotary frequencies theta^(-2k/D), k < D/2 (when rope)
 };
 
 // ------------------------------------------------------------------ Delta
@@ -95,6 +90,24 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdParams p, long rows_per_b
 // +inf so that their recomputed probabilities are exactly 0.
 __device__ __forceinline__ float lse_to_log2(float l) {
   return l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
+}
+
+// Turn an MFMA accumulator over dims (acc[db] holds dims 32*db + 8*(r/4) +
+// 4*g + r%4 of one row, the row being the lane's query or key at position pos)
+// back by the rotary angle of that position: dims k and k + D/2 sit in blocks
+// db and db + NDB/2 of the same lane and register.
+template <int NDB>
+__device__ __forceinline__ void rope_back(f32x16 (&acc)[NDB], int pos, const double* f, int g) {
+#pragma unroll
+  for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int k = 32 * db + 8 * (r >> 2) + 4 * g + (r & 3);
+      float lo = acc[db][r], hi = acc[db + NDB / 2][r];
+      rope_turn(lo, hi, rope_cos_sin(pos, f[k]), true);
+      acc[db][r] = lo;
+      acc[db + NDB / 2][r] = hi;
+    }
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -265,24 +278,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // The same for a role-B wave that has written the dS panel: its global stores
-  // share the load counter and were issued after the loads waited for, so the
-  // PANEL_STORES stores of each of the last `ns` steps (0..3) may stay in flight.
-  constexpr int PANEL_STORES = 2;
-  auto wait_ring_b = [&](auto N, int ns) {
-    constexpr int n = decltype(N)::value * LOADS;
-    if (ns == 0)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
-    else if (ns == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n + PANEL_STORES) : "memory");
-    else if (ns == 2)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n + 2 * PANEL_STORES) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n + 3 * PANEL_STORES) : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-
   // per-lane LDS offsets (elements)
   // operand of the score products: row ln, chunk 2*ks+g = slot 2*(ks ^ qx) + (g ^ (swz & 1))
   const int qx = swz<D>(ln) >> 1, qbase = ln * D + ((g ^ (swz<D>(ln) & 1)) << 3);
@@ -346,43 +341,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     }
   };
 
-  // ---- dS panel (role B, when p.ds is set): the bf16 dS of query tile tq and
-  // this wave's 32 keys go to sub-block tq % 8 (2 KiB) of block (query block
-  // tq / 8, key group kg).  Lane (ln, g) holds queries 16*kk + 8*m + 4*g + (0..3)
-  // of key ln in pk[kk] elements 4m..4m+3; one exchange with lane ln + 32*(1-g)
-  // gives it queries 16*kk + 8*g + (0..7), which it writes as 16 bytes at chunk
-  // 64*kk + lane of the sub-block: two stores per step, each 1 KiB contiguous.
-  // Query tiles come in decreasing order, so the block prefix of the current
-  // query block is kept and walked down.
-  const int kg = j0 / kPanelK + kw;
-  int pan_qb = -1, pan_pref = 0;
-  auto panel_store = [&](int tq, const bf16x8* pk) -> bool {  // true: PANEL_STORES stores issued
-    const int qb = tq / (kPanelQ / BQ);
-    if (pan_qb < 0 || qb > pan_qb) {
-      pan_pref = panel_prefix(p.qs, p.ks, p.causal, qb, lane);
-      pan_qb = qb;
-    }
-    while (pan_qb > qb) {
-      --pan_qb;
-      pan_pref -= panel_count(p.qs, p.ks, p.causal, pan_qb);
-    }
-    const int pos = panel_pos(panel_list(p.qs, p.ks, p.causal, qb), kg);
-    if (pos < 0) return false;  // no key of the group is allowed for the query block: nothing is read back
-    const int sub = tq % (kPanelQ / BQ);
-    uint16_t* dst = p.ds + ((long)bh * p.ds_per_bh + pan_pref + pos) * kPanelBlock + sub * (kPanelK * BQ) + lane * 8;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const u32x4 u = __builtin_bit_cast(u32x4, pk[kk]);
-      // g = 0 keeps queries 0..3 (u0, u1) and takes 4..7 from g = 1; g = 1 keeps 12..15 (u2, u3) and
-      // takes 8..11 from g = 0 (offsets within the 16)
-      const uint32_t x0 = g ? u[0] : u[2], x1 = g ? u[1] : u[3];
-      const uint32_t y0 = __shfl_xor(x0, 32), y1 = __shfl_xor(x1, 32);
-      const u32x4 o = g ? u32x4{y0, y1, u[2], u[3]} : u32x4{u[0], u[1], y0, y1};
-      *reinterpret_cast<u32x4*>(dst + kk * (64 * 8)) = o;
-    }
-    return true;
-  };
-
   const float c = p.c;
   constexpr float NEG_INF = -__builtin_inff();
   using RA = std::integral_constant<int, 0>;
@@ -423,8 +381,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 
   // ---- role B, step t: dP(t) (into dp_nx) interleaved with dS(t-1) from P(t-1)
   // and dP(t-1) (in dp_cur); dK^T += Q(t-1)^T dS(t-1).  PSTAGE = stage of t-1.
-  // Returns whether dS(t-1) was written to the panel.
-  auto step_b = [&](int stage, int pstage, auto DO_DP, int t, f32x16& dp_cur, f32x16& dp_nx) -> bool {
+  auto step_b = [&](int stage, int pstage, auto DO_DP, int t, f32x16& dp_cur, f32x16& dp_nx) {
     constexpr bool do_dp = decltype(DO_DP)::value;  // false: last step, no tile t
     const bool prev = t > 0;
     float dsv[16];
@@ -442,10 +399,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     }
     bf16x8 pk[2];
     pack16(dsv, pk);
-    const bool wrote = p.ds != nullptr && prev && panel_store(tile_of(t - 1), pk);
     // at step 0 the zeros multiply tile 0's Q (resident, finite) rather than a stage never loaded
     accumulate(RB{}, prev ? pstage : stage, pk);
-    return wrote;
   };
 
   // Wave 0, which loads the per-row statistics, rewrites the LSE of a resident
@@ -478,15 +433,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
         ca = classify(0);
         scores(RA{}, 0, sa);
       }
-      int st = 0;        // stage of tile t
-      int panel_hist = 0;  // role B: bit i set if step t-1-i wrote the dS panel
+      int st = 0;  // stage of tile t
       auto body = [&](int t, f32x16& x_cur, int& c_cur, f32x16& x_nx, int& c_nx) {
-        if (t > 0) {  // tile t+1 resident; all past step t-1
-          if constexpr (R == 1)
-            wait_ring_b(std::integral_constant<int, AHEAD>{}, __builtin_popcount(panel_hist & 7));
-          else
-            wait_ring(std::integral_constant<int, AHEAD>{});
-        }
+        if (t > 0) wait_ring(std::integral_constant<int, AHEAD>{});  // tile t+1 resident; all past step t-1
         const int sp = st == 0 ? NST - 1 : st - 1;
         const int sf = st >= 2 ? st - 2 : st + NST - 2;
         issue_tile(sf, t + NST - 2);
@@ -494,8 +443,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
           to_log2(st + 1 == NST ? 0 : st + 1);  // tile t+1, read from step t+1 on
           step_a(st, t, x_cur, c_cur, x_nx, c_nx);
         } else {
-          const bool wrote = step_b(st, sp, std::true_type{}, t, x_cur, x_nx);
-          panel_hist = (panel_hist << 1) | (wrote ? 1 : 0);
+          step_b(st, sp, std::true_type{}, t, x_cur, x_nx);
         }
         st = st + 1 == NST ? 0 : st + 1;
       };
@@ -527,6 +475,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   }
 
   if (!key_ok || nt == 0) return;
+  // dK of rotated keys turned back by the key's position: the gradient with respect to the unrotated row
+  // (the rotation is linear, so turning each call's contribution before it is added is exact)
+  if (role == 1 && p.rope) rope_back(acc, kpos, p.f, g);
   float* dst = (role == 0 ? p.dv : p.dk) + b * p.k_bstride + (long)h * D_ + (long)krow * p.rs;
   const float mul = role == 0 ? 1.f : p.scale;
 #pragma unroll
@@ -777,193 +728,7 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
   }
 
   if (!row_ok || nt == 0) return;
-  float* dqp = p.dq + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = db * 32 + 8 * q4 + 4 * g;
-      f32x4 v4 = *reinterpret_cast<f32x4*>(dqp + d0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] += p.scale * dqa[db][4 * q4 + e];
-      *reinterpret_cast<f32x4*>(dqp + d0) = v4;
-    }
-}
-
-// ------------------------------------------------------------------ dQ from the dS panel
-// dQ = scale * dS K once the key-major pass has left dS in the panel: one
-// workgroup = 8 waves = one 256-row query block (the panel's), two waves per
-// SIMD; each wave owns 32 query rows and their dQ^T accumulator.  Per key group
-// of the block's list, the 32-key K tile and the 16 KiB panel block stream
-// through a 6-stage direct-to-LDS ring (the panel is read once, so this pass is
-// bound by HBM bandwidth); dQ^T += K^T dS^T takes both operands by transpose
-// reads: K^T from the row-major K tile, dS^T from the block's [keys][queries]
-// half.  A wave skips a group none of whose keys its rows may see: the
-// key-major pass never visits such a (tile, group) pair, and its dS is zero.
-template <int D>
-struct DqsCfg {
-  static constexpr int NW = 8, BQ = kPanelQ, BK = kPanelK, NT = 64 * NW, NST = 6;
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per K row
-  static constexpr int RPI = 64 / CPR;               // K rows one direct-to-LDS load covers
-  static constexpr int NLK = BK / RPI;               // loads per K tile (waves 0 .. NLK-1, one each)
-  static constexpr int NLS = 2 * BK * 128 * 2 / 1024;  // loads per panel block (16 per 16 KiB)
-  static constexpr int NSW = NLS / NW;               // panel loads per wave
-  static constexpr int KT = BK * D, ST = 2 * BK * 128;  // elements per K tile, per panel block
-  static_assert(NLK <= NW && NSW * NW == NLS, "unsupported tile");
-};
-
-template <int D>
-__global__ __launch_bounds__(512, 1) void dqs_kernel(BwdParams p) {
-  using Cfg = DqsCfg<D>;
-  constexpr int BQ = Cfg::BQ, BK = Cfg::BK, CPR = Cfg::CPR, NST = Cfg::NST, RPI = Cfg::RPI;
-  constexpr int NDB = D / 32, KT = Cfg::KT, ST = Cfg::ST;
-  // stage s: K tile at KS[s][0], panel block at KS[s][KT]
-  __shared__ __attribute__((aligned(16))) uint16_t KS[NST][KT + ST];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5;
-
-  const int work = xcd_remap(blockIdx.x, gridDim.x, p.nblk);
-  const int bh = work / p.nblk;
-  const int qb = p.nblk - 1 - work % p.nblk;  // longest query blocks first
-  const int b = bh / p.H, h = bh % p.H;
-  const int D_ = D;
-  const uint16_t* kp = p.k + b * p.k_bstride + (long)h * D_;
-
-  const int i0 = qb * BQ;
-  const int w0 = i0 + 32 * w, w1 = min(w0 + 32, p.Sq);
-  const bool wave_live = w0 < w1;
-  int qmin_w = 0, qmax_w = -1;
-  if (wave_live) seg_range(p.qs, w0, w1, qmin_w, qmax_w);
-
-  const PanelList L = panel_list(p.qs, p.ks, p.causal, qb);
-  const int nt = L.nA + L.nB;
-  auto group_of = [&](int t) { return t < L.nA ? t : L.tB0 + (t - L.nA); };
-  const int pref = panel_prefix(p.qs, p.ks, p.causal, qb, lane);
-  const uint16_t* blk0 = p.ds + ((long)bh * p.ds_per_bh + pref) * kPanelBlock;
-
-  f32x16 dqa[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) dqa[db] = f32x16{};
-
-  // ---- direct global -> LDS loads.  K: wave w < NLK moves rows [RPI*w, +RPI)
-  // (rows past the end of the keys load the last key row; their dS is zero).
-  // Panel: the block lands as two row-major [32 keys][128 queries] halves (rows
-  // 0..63, half = row / 32); wave w moves rows [4*(w + NW*i), +4), i = 0 ..
-  // NSW-1, lane i filling slot i % 16 of its row, i.e. query chunk c = slot ^
-  // swz(row) (queries 8c .. 8c+7 of the half).  The key-major pass wrote that
-  // chunk of key n as the 16 bytes at chunk 64*kk + 32*gg + n of sub-block
-  // 4*half + c/4, with kk = (c % 4) / 2, gg = c % 2.
-  const int kdma_row = RPI * w + lane / CPR, kdma_slot = lane % CPR;
-  const long kdma_off = (long)kdma_row * p.rs + ((kdma_slot ^ swz<D>(kdma_row)) << 3);
-  long sdma_off[Cfg::NSW];
-#pragma unroll
-  for (int i = 0; i < Cfg::NSW; ++i) {
-    const int row = 4 * (w + Cfg::NW * i) + lane / 16;
-    const int n = row & 31, half = row >> 5, c = (lane % 16) ^ swz<128>(row);
-    const int sub = 4 * half + (c >> 2), kk = (c & 3) >> 1, gg = c & 1;
-    sdma_off[i] = (long)sub * (BK * 32) + (64 * kk + 32 * gg + n) * 8;
-  }
-  auto issue_tile = [&](auto STAGE, int t) {
-    constexpr int stage = decltype(STAGE)::value;
-    const int tt = t < nt ? t : nt - 1;  // past the end: reload the last tile into a stage nobody reads
-    if (w < Cfg::NLK) {
-      const int j0 = group_of(tt) * BK;
-      long off = (long)j0 * p.rs + kdma_off;
-      if (j0 + BK > p.Sk) {
-        const int j = min(j0 + kdma_row, p.Sk - 1);
-        off = (long)j * p.rs + ((kdma_slot ^ swz<D>(kdma_row)) << 3);
-      }
-      dma16(kp + off, &KS[stage][RPI * w * D]);
-    }
-    const uint16_t* blk = blk0 + (long)tt * kPanelBlock;
-#pragma unroll
-    for (int i = 0; i < Cfg::NSW; ++i) dma16(blk + sdma_off[i], &KS[stage][KT + 4 * (w + Cfg::NW * i) * 128]);
-  };
-  // loads per tile: NSW for every wave, one more for waves 0 .. NLK-1
-  auto ring_sync = [&](auto N) {  // at most N tiles of this wave's loads in flight; barrier
-    constexpr int n = decltype(N)::value;
-    if (w < Cfg::NLK)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n * (Cfg::NSW + 1)) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n * Cfg::NSW) : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-
-  // transpose-read offsets: rows 8*half + trow (+16 per k-step) and 32 columns
-  // per block; K^T blocks db = 0 .. NDB-1, dS^T the wave's 32 queries in half w/4
-  int tofs[2][NDB], sofs[2];
-  {
-    const int trow = 4 * g + ((lane & 15) >> 2);
-    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int col = 32 * db + tcol;
-        tofs[half][db] = tile_off<D>(8 * half + trow, col >> 3) + (col & 7);
-      }
-      const int col = 32 * (w & 3) + tcol;
-      sofs[half] = KT + (w >> 2) * (BK * 128) + tile_off<128>(8 * half + trow, col >> 3) + (col & 7);
-    }
-  }
-
-  auto step = [&](auto STAGE, int t) {
-    constexpr int stage = decltype(STAGE)::value;
-    constexpr int fstage = (stage + NST - 1) % NST;
-    ring_sync(std::integral_constant<int, NST - 2>{});  // tile t resident; all done with stage (t-1) % NST
-    issue_tile(std::integral_constant<int, fstage>{}, t + NST - 1);
-    bool live = wave_live;
-    if (p.causal) {
-      const int j0 = group_of(t) * BK;
-      int kmn, kmx;
-      seg_range(p.ks, j0, min(j0 + BK, p.Sk), kmn, kmx);
-      live = live && kmn <= qmax_w;
-    }
-    if (live) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const u32x2 slo = ds_read_tr16(&KS[stage][sofs[0] + 16 * kk * 128]);
-        const u32x2 shi = ds_read_tr16(&KS[stage][sofs[1] + 16 * kk * 128]);
-        const u32x4 bs = {slo[0], slo[1], shi[0], shi[1]};
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x2 lo = ds_read_tr16(&KS[stage][tofs[0][db] + 16 * kk * D]);
-          const u32x2 hi = ds_read_tr16(&KS[stage][tofs[1][db] + 16 * kk * D]);
-          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-          dqa[db] = mfma32(as_bf16x8(a), as_bf16x8(bs), dqa[db]);
-        }
-      }
-    }
-  };
-
-  if (nt > 0) {
-    static_assert(NST == 6, "the loop below is unrolled for a ring of 6 stages");
-    issue_tile(std::integral_constant<int, 0>{}, 0);
-    issue_tile(std::integral_constant<int, 1>{}, 1);
-    issue_tile(std::integral_constant<int, 2>{}, 2);
-    issue_tile(std::integral_constant<int, 3>{}, 3);
-    issue_tile(std::integral_constant<int, 4>{}, 4);
-    for (int t = 0; t < nt; t += 6) {
-      step(std::integral_constant<int, 0>{}, t);
-      if (t + 1 >= nt) break;
-      step(std::integral_constant<int, 1>{}, t + 1);
-      if (t + 2 >= nt) break;
-      step(std::integral_constant<int, 2>{}, t + 2);
-      if (t + 3 >= nt) break;
-      step(std::integral_constant<int, 3>{}, t + 3);
-      if (t + 4 >= nt) break;
-      step(std::integral_constant<int, 4>{}, t + 4);
-      if (t + 5 >= nt) break;
-      step(std::integral_constant<int, 5>{}, t + 5);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // retire the trailing (unused) loads
-  }
-
-  const int qrow = w0 + (lane & 31);
-  if (qrow >= p.Sq || nt == 0) return;
+  if (p.rope) rope_back(dqa, qpos, p.f, g);  // gradient with respect to the unrotated query row
   float* dqp = p.dq + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -979,14 +744,6 @@ __global__ __launch_bounds__(512, 1) void dqs_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ launchers
 static Seg to_seg(const SegArg& s) { return Seg{s.s0, s.l0, s.s1, s.n}; }
-
-int64_t panel_blocks(const SegArg& qs, const SegArg& ks, int causal) {
-  const Seg q = to_seg(qs), k = to_seg(ks);
-  const int nqb = (q.n + kPanelQ - 1) / kPanelQ;
-  int64_t total = 0;
-  for (int qb = 0; qb < nqb; ++qb) total += panel_count(q, k, causal, qb);
-  return total;
-}
 
 static BwdParams make_params(const BwdArgs& a) {
   BwdParams p;
@@ -1006,8 +763,8 @@ static BwdParams make_params(const BwdArgs& a) {
   p.row_bstride = (long)a.q_batch_rows * a.Hs;
   p.H = a.H;
   p.Hs = a.Hs;
-  p.ds = a.ds;
-  p.ds_per_bh = a.ds_per_bh;
+  p.rope = a.rope;
+  for (int k = 0; k < 64; ++k) p.f[k] = a.rope && k < a.D / 2 ? a.inv_freq[k] : 0.0;
   p.Sq = a.Sq;
   p.Sk = a.Sk;
   p.qs = to_seg(a.qs);
@@ -1046,19 +803,6 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(dkdv_kernel<64>, grid, block, 0, stream, p);
   else
     hipLaunchKernelGGL(dkdv_kernel<128>, grid, block, 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_dqs(const BwdArgs& a, hipStream_t stream) {
-  BwdParams p = make_params(a);
-  p.nblk = (a.Sq + kPanelQ - 1) / kPanelQ;
-  const long nwg = (long)a.B * a.H * p.nblk;
-  if (nwg == 0 || a.Sk == 0) return hipSuccess;
-  dim3 grid((unsigned)nwg), block(DqsCfg<128>::NT);
-  if (a.D == 64)
-    hipLaunchKernelGGL(dqs_kernel<64>, grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL(dqs_kernel<128>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -177,66 +177,59 @@ __host__ __device__ __forceinline__ void causal_key_ranges(const Seg& k, int qma
   e1 = k.l0 + (int)n1;
 }
 
-// ---- dS panel: the bf16 dS of one backward call, kept in HBM between the
-// key-major pass that forms it and the query-major pass that contracts it with
-// K.  Per (batch, head) it holds one 16 KiB block for every pair (query block of
-// kPanelQ rows, key group of kPanelK keys) the query block may see, query
-// blocks in order; within a query block the key groups come in the order the
-// query-major pass visits them: the groups covering [0, e0), then those
-// covering [b1, e1) not already counted (causal_key_ranges of the block's
-// largest position; every group under the full mask).  A block is eight 2 KiB
-// sub-blocks, one per 32-query tile of the query block, each holding the tile's
-// dS for the group's 32 keys in the order the key-major pass produces it (see
-// the dK/dV kernel); the dQ pass gathers it into row-major tiles.
-constexpr int kPanelQ = 256, kPanelK = 32;
-constexpr long kPanelBlock = (long)kPanelQ * kPanelK;  // elements per block
-
-struct PanelList {
-  int nA, tB0, nB;  // groups [0, nA), then [tB0, tB0 + nB)
-};
-
-__host__ __device__ __forceinline__ PanelList panel_list(const Seg& qs, const Seg& ks, int causal, int qb) {
-  int e0 = ks.n, b1 = ks.n, e1 = ks.n;
-  if (causal) {
-    const int i0 = qb * kPanelQ, i1 = i0 + kPanelQ < qs.n ? i0 + kPanelQ : qs.n;
-    int mn, mx;
-    seg_range(qs, i0, i1, mn, mx);
-    causal_key_ranges(ks, mx, e0, b1, e1);
-  }
-  PanelList L;
-  L.nA = (e0 + kPanelK - 1) / kPanelK;
-  int t0 = b1 / kPanelK, t1 = (e1 + kPanelK - 1) / kPanelK;
-  if (e1 <= b1) t1 = t0;
-  if (t0 < L.nA) t0 = L.nA;
-  L.tB0 = t0;
-  L.nB = t1 > t0 ? t1 - t0 : 0;
-  return L;
+// ---- rotary position embedding (Llama "rotate-half"): dims k and k + D/2 of a
+// row at position p turn by phi = p * f_k, f_k = theta^(-2k/D).  The angle is
+// formed in fp64 (positions reach 2^31, where an fp32 angle is off by a large
+// fraction of a radian) and its cosine and sine are rounded to fp32; the
+// rotation itself is fp32 with one rounding to the output type.  Every kernel
+// that rotates uses these functions, so a row rotated in any of them has the
+// same bits.
+//
+// cos and sin in fp64 for a >= 0: Cody-Waite reduction a = n pi/2 + r with a
+// two-part pi/2 (|r| <= pi/4; the product n * hi is exact to the last place of
+// r by fma), then the Taylor series of sin r to r^15 and of cos r to r^16 (the
+// first omitted terms are below 1e-16 relative on |r| <= pi/4), and the
+// quadrant n mod 4 swaps and negates them.  Short and register-light, unlike
+// a general sincos that must also handle huge arguments.
+__device__ __forceinline__ float2 rope_cos_sin(int pos, double f) {
+  const double a = (double)pos * f;
+  constexpr double kPio2Hi = 1.5707963267948966;      // pi/2 rounded to double
+  constexpr double kPio2Lo = 6.123233995736766e-17;   // pi/2 - kPio2Hi
+  constexpr double k2OverPi = 0.6366197723675814;
+  const double n = __builtin_rint(a * k2OverPi);
+  double r = __builtin_fma(-n, kPio2Hi, a);
+  r = __builtin_fma(-n, kPio2Lo, r);
+  const double z = r * r;
+  // 1/k! for the odd (sin) and even (cos) terms
+  double sp = 7.647163731819816e-13;                  // 1/15!
+  sp = __builtin_fma(sp, -z, 1.6059043836821613e-10); // 1/13!
+  sp = __builtin_fma(sp, -z, 2.505210838544172e-08);  // 1/11!
+  sp = __builtin_fma(sp, -z, 2.7557319223985893e-06); // 1/9!
+  sp = __builtin_fma(sp, -z, 0.0001984126984126984);  // 1/7!
+  sp = __builtin_fma(sp, -z, 0.008333333333333333);  // 1/5!
+  sp = __builtin_fma(sp, -z, 0.16666666666666666); // 1/3!
+  const double sn = __builtin_fma(-r * z, sp, r);
+  double cp = 4.779477332387385e-14;                  // 1/16!
+  cp = __builtin_fma(cp, -z, 1.1470745597729725e-11); // 1/14!
+  cp = __builtin_fma(cp, -z, 2.08767569878681e-09);   // 1/12!
+  cp = __builtin_fma(cp, -z, 2.755731922398589e-07);  // 1/10!
+  cp = __builtin_fma(cp, -z, 2.48015873015873e-05);   // 1/8!
+  cp = __builtin_fma(cp, -z, 0.001388888888888889);  // 1/6!
+  cp = __builtin_fma(cp, -z, 0.041666666666666664); // 1/4!
+  cp = __builtin_fma(cp, -z, 0.5);                    // 1/2!
+  const double cs = __builtin_fma(-z, cp, 1.0);
+  const int quad = (int)((long long)n & 3);
+  const double c = (quad & 1) ? sn : cs, s = (quad & 1) ? cs : sn;
+  return make_float2((float)((quad == 1 || quad == 2) ? -c : c), (float)((quad >= 2) ? -s : s));
 }
 
-__host__ __device__ __forceinline__ int panel_count(const Seg& qs, const Seg& ks, int causal, int qb) {
-  const PanelList L = panel_list(qs, ks, causal, qb);
-  return L.nA + L.nB;
-}
-
-// Index of key group kg in a query block's list, or -1 if the block sees none
-// of its keys.
-__host__ __device__ __forceinline__ int panel_pos(const PanelList& L, int kg) {
-  if (kg < L.nA) return kg;
-  const int u = kg - L.tB0;
-  return (u >= 0 && u < L.nB) ? L.nA + u : -1;
-}
-
-// Blocks of query blocks [0, qb) of one (batch, head), summed by the 64 lanes
-// of a wave (all lanes must be active; the result is uniform).
-__device__ __forceinline__ int panel_prefix(const Seg& qs, const Seg& ks, int causal, int qb, int lane) {
-  int s = 0;
-  for (int q0 = 0; q0 < qb; q0 += 64) {
-    const int q = q0 + lane;
-    if (q < qb) s += panel_count(qs, ks, causal, q);
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-  return __builtin_amdgcn_readfirstlane(s);
+// (lo, hi) = dims (k, k + D/2) turned by the angle whose (cos, sin) is cs;
+// inverse turns by minus that angle (the transpose, for gradients).
+__device__ __forceinline__ void rope_turn(float& lo, float& hi, float2 cs, bool inverse) {
+  const float sn = inverse ? -cs.y : cs.y;
+  const float l = lo, h = hi;
+  lo = __builtin_fmaf(l, cs.x, -h * sn);
+  hi = __builtin_fmaf(h, cs.x, l * sn);
 }
 
 // Key rows a query at position qpos may see, as [0, lim0) U [l0, lim1) of the

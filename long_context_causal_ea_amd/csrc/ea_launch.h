@@ -25,6 +25,9 @@ struct FwdArgs {
   int o_bf16;
   int merge;  // 1: merge into (o, lse) as an fp32 accumulator instead of overwriting
   float scale;
+  int rope;             // 1: q rows are turned by their rotary angles in registers before use
+  uint16_t* q_rot;      // when rope: the turned q rows are also written here (may be null)
+  double inv_freq[64];  // when rope: theta^(-2k/D), k < D/2
 };
 
 struct BwdArgs {
@@ -45,8 +48,8 @@ struct BwdArgs {
   int causal;
   int o_bf16;
   float scale;
-  uint16_t* ds;   // dS panel for these B*H heads, or null (dQ by recomputation)
-  int ds_per_bh;  // panel blocks per (batch, head)
+  int rope;             // 1: q, k are rotated rows; dq, dk contributions are turned back before they are added
+  double inv_freq[64];  // when rope: theta^(-2k/D), k < D/2
 };
 
 struct MergeArgs {
@@ -82,13 +85,15 @@ struct RopeArgs {
   double inv_freq[64];  // theta^(-2k/D), k < D/2
 };
 
+// Workgroup shapes of the elementwise launches (the host bounds their grids).
+constexpr int kXentBlock = 512;        // threads per workgroup, one workgroup per logits row
+constexpr int kRopeBlock = 256;        // threads per workgroup
+constexpr int kRopeRowsPerBlock = 4;   // token rows per workgroup
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_dqs(const BwdArgs& a, hipStream_t stream);
-// dS panel blocks per (batch, head) for these query/key segments (16 KiB each).
-int64_t panel_blocks(const SegArg& qs, const SegArg& ks, int causal);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_xent(const XentArgs& a, hipStream_t stream);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);

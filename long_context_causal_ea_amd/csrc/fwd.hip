@@ -24,6 +24,9 @@
 //    pair), FULL (all allowed, no mask work) or PARTIAL (element mask; also
 //    ragged key tails).  Tiles no query of the workgroup may see are never
 //    loaded.
+//  - With a rotary base, each lane turns its query row in registers right
+//    after loading it (dims k and k + D/2 are in the same lane) and can write
+//    the turned row out for the backward; keys arrive already turned.
 #include <type_traits>
 
 #include "ea_device.h"
@@ -43,6 +46,9 @@ struct FwdParams {
   Seg qs, ks;
   int causal, o_bf16, merge;
   float scale, c;  // c = scale * log2(e)
+  int rope;        // 1: turn the q rows by their rotary angles after loading them
+  uint16_t* q_rot; // when rope: the turned rows are also written here (may be null)
+  double f[64];    // rotary frequencies theta^(-2k/D), k < D/2
 };
 
 #ifndef EA_FWD_NW
@@ -112,6 +118,28 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
     for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qf[ks]));
   }
   const int qpos = seg_pos(p.qs, row_ok ? qrow : (p.Sq - 1));
+  if (p.rope) {
+    // rotary embedding of the row in registers: qf[ks] holds dims 16*ks + 8*g + e, and dims k and k + D/2
+    // are packs ks and ks + NKS/2 of the same lane
+#pragma unroll
+    for (int ks = 0; ks < NKS / 2; ++ks) {
+      const u32x4 ul = __builtin_bit_cast(u32x4, qf[ks]), uh = __builtin_bit_cast(u32x4, qf[ks + NKS / 2]);
+      float lo[8], hi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] = __uint_as_float((e & 1) ? (ul[e >> 1] & 0xffff0000u) : (ul[e >> 1] << 16));
+        hi[e] = __uint_as_float((e & 1) ? (uh[e >> 1] & 0xffff0000u) : (uh[e >> 1] << 16));
+        rope_turn(lo[e], hi[e], rope_cos_sin(qpos, p.f[16 * ks + 8 * g + e]), false);
+      }
+      qf[ks] = pack_bf16x8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
+      qf[ks + NKS / 2] = pack_bf16x8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
+    }
+    if (p.q_rot != nullptr && row_ok) {  // the turned rows for the backward
+      u32x4* dst = reinterpret_cast<u32x4*>(p.q_rot + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs + 8 * g);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) dst[2 * ks] = __builtin_bit_cast(u32x4, qf[ks]);
+    }
+  }
   const KeyWindow kwin = key_window(p.ks, qpos, p.causal);
 
   // ---- position ranges of the workgroup's and this wave's valid rows
@@ -397,6 +425,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.merge = a.merge;
   p.scale = a.scale;
   p.c = a.scale * kLog2e;
+  p.rope = a.rope;
+  p.q_rot = a.rope ? a.q_rot : nullptr;
+  for (int k = 0; k < 64; ++k) p.f[k] = a.rope && k < a.D / 2 ? a.inv_freq[k] : 0.0;
   const int BQ = FwdCfg<128>::BQ;
   p.nqb = (a.Sq + BQ - 1) / BQ;
   const long nwg = (long)a.B * a.H * p.nqb;

@@ -11,19 +11,19 @@
 //
 // HBM-bound elementwise pass.  A workgroup takes kRopeRows token rows (all H
 // heads of each).  The D/2 angles of a row are shared by its heads: they are
-// formed once per row in fp64 (p * theta^(-2k/D) with the frequencies computed
-// on the host in fp64, reduced modulo 2 pi with a two-part constant, then
-// sin/cos in fp64) and kept in LDS as fp32 pairs; positions reach 2^31, where an
-// fp32 angle would be off by a large fraction of a radian.  The rotation itself
-// is fp32 with one rounding to the output type.  Each thread handles the two
-// 16-byte chunks that hold x_k .. and x_{k+D/2} .. of one head.
+// formed once per row (rope_cos_sin: fp64 angle from frequencies computed on
+// the host in fp64, fp32 cosine and sine) and kept in LDS.  The rotation
+// (rope_turn) is fp32 with one rounding to the output type; the attention
+// kernels that rotate query rows in registers use the same two functions.  Each
+// thread handles the two 16-byte chunks that hold x_k .. and x_{k+D/2} .. of
+// one head.
 #include "ea_device.h"
 #include "ea_launch.h"
 
 namespace ea {
 
-constexpr int kRopeThreads = 256;
-constexpr int kRopeRows = 4;
+constexpr int kRopeThreads = kRopeBlock;
+constexpr int kRopeRows = kRopeRowsPerBlock;
 
 struct RopeParams {
   const void* x;
@@ -78,16 +78,9 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
   for (int idx = tid; idx < kRopeRows * HALF; idx += kRopeThreads) {
     const int r = idx / HALF, k = idx % HALF, gr = row0 + r;
     if (gr >= p.rows) continue;
-    const int pos = seg_pos(p.seg, gr % p.S);
-    const double a = (double)pos * p.f[k];
-    constexpr double kTwoPiHi = 6.283185307179586232;     // 2 pi rounded to double
-    constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2 pi - kTwoPiHi
-    const double n = __builtin_rint(a * (1.0 / 6.283185307179586232));
-    double red = __builtin_fma(-n, kTwoPiHi, a);
-    red = __builtin_fma(-n, kTwoPiLo, red);
-    double s, c;
-    sincos(red, &s, &c);
-    cs[r][k + k / EPC] = make_float2((float)c, (float)(p.inverse ? -s : s));
+    float2 t = rope_cos_sin(seg_pos(p.seg, gr % p.S), p.f[k]);
+    if (p.inverse) t.y = -t.y;  // the transpose: turn by minus the angle
+    cs[r][k + k / EPC] = t;
   }
   __syncthreads();
 
@@ -104,15 +97,10 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
     float lo[EPC], hi[EPC];
     IO::load(src, lo);
     IO::load(src + HALF * ESZ, hi);
-    float ylo[EPC], yhi[EPC];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      const float2 t = cs[r][c * (EPC + 1) + e];
-      ylo[e] = __builtin_fmaf(lo[e], t.x, -hi[e] * t.y);
-      yhi[e] = __builtin_fmaf(hi[e], t.x, lo[e] * t.y);
-    }
-    IO::store(dst, ylo);
-    IO::store(dst + HALF * ESZ, yhi);
+    for (int e = 0; e < EPC; ++e) rope_turn(lo[e], hi[e], cs[r][c * (EPC + 1) + e], false);
+    IO::store(dst, lo);
+    IO::store(dst + HALF * ESZ, hi);
   }
 }
 

@@ -33,10 +33,7 @@ struct XentParams {
   float g;
 };
 
-#ifndef EA_XENT_THREADS
-#define EA_XENT_THREADS 512
-#endif
-constexpr int kXentThreads = EA_XENT_THREADS;
+constexpr int kXentThreads = kXentBlock;
 
 // (m, s) stands for s * exp(m): merge another such pair into it
 __device__ __forceinline__ void combine(float& m, float& s, float m2, float s2) {

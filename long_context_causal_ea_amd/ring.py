@@ -13,10 +13,13 @@ rule on global positions selects, per step, the full, causal or half blocks.
 ``DenseCausal`` is the whole-sequence case: one forward and one backward
 call over positions 0..S-1.
 
-With ``rope_theta`` set, both drivers take unrotated Q and K: the forward first
-rotates them by their global positions (``ea_rope`` into buffers the driver
-owns) and the backward rotates dQ and dK back (the transpose, in place), so the
-gradients are with respect to the unrotated inputs.
+With ``rope_theta`` set, both drivers take unrotated Q and K.  The forward
+rotates K by its global positions (``ea_rope`` into a buffer the driver owns)
+and hands Q unrotated to ``ea_attn_fwd_rope``, which turns each query row in
+registers and writes the turned rows once for the backward; the backward
+(``ea_attn_bwd_rope``) turns each dQ and dK contribution back before adding it,
+so the gradients are with respect to the unrotated inputs and no separate
+rotation pass over Q, dQ or dK is needed.
 
 All buffers are allocated when the driver is built; ``forward`` and
 ``backward`` enqueue work on the given stream (default: the current one) and
@@ -92,17 +95,6 @@ def _zero(stream, *ts):
             t.zero_()
 
 
-def _panel(dev, per_head: int, heads: int, cap_bytes):
-    """Workspace for the dS panel: all ``heads`` (batch, head) slices if they fit ``cap_bytes``, else as many
-    whole slices as fit (the library then runs the heads in groups); None without a cap (dq by recomputation)."""
-    if cap_bytes is None or per_head == 0:
-        return None
-    n = min(heads, int(cap_bytes) // per_head)
-    if n < 1:
-        raise ValueError(f"panel_bytes {cap_bytes} below one head's dS panel ({per_head} bytes)")
-    return torch.empty(n * per_head, dtype=torch.uint8, device=dev)
-
-
 def capture_step(driver, do):
     """Record one whole ``driver.step(do)`` (rotations, forward, merges, zeroing, backward) as a HIP graph.
 
@@ -117,13 +109,9 @@ def capture_step(driver, do):
 
 
 class DenseCausal:
-    """Dense (whole-sequence) attention of one GPU: forward, then backward into fp32 gradients.
+    """Dense (whole-sequence) attention of one GPU: forward, then backward into fp32 gradients."""
 
-    panel_bytes: None computes dq by recomputing the scores; a byte count keeps the bf16 dS in a workspace of at
-    most that size (``ea_attn_bwd_ws``), allocated here once.
-    """
-
-    def __init__(self, q, k, v, causal=True, scale=None, o_dtype=torch.float32, rope_theta=None, panel_bytes=None):
+    def __init__(self, q, k, v, causal=True, scale=None, o_dtype=torch.float32, rope_theta=None):
         B, S, H, D = q.shape
         self.rope_theta = rope_theta
         self.q_in, self.k_in = q, k
@@ -143,24 +131,24 @@ class DenseCausal:
         self.dv = torch.empty_like(self.dk)
         self.q_seg = [0, S]
         self.k_seg = [0, k.shape[1]]
-        self.panel = _panel(dev, L.ea_attn_bwd_ws_bytes(S, k.shape[1], self.q_seg, self.k_seg, causal), B * H,
-                            panel_bytes)
 
     def forward(self, stream=None):
-        if self.rope_theta is not None:
-            L.ea_rope(self.q_in, self.q, self.q_seg, self.rope_theta, stream=stream)
-            L.ea_rope(self.k_in, self.k, self.k_seg, self.rope_theta, stream=stream)
-        L.ea_attn_fwd(self.q, self.k, self.v, self.o, self.lse, self.q_seg, self.k_seg, self.causal, self.scale,
-                      stream)
+        if self.rope_theta is None:
+            L.ea_attn_fwd(self.q, self.k, self.v, self.o, self.lse, self.q_seg, self.k_seg, self.causal, self.scale,
+                          stream)
+            return
+        L.ea_rope(self.k_in, self.k, self.k_seg, self.rope_theta, stream=stream)
+        L.ea_attn_fwd_rope(self.q_in, self.k, self.v, self.o, self.lse, self.q_seg, self.k_seg, self.rope_theta,
+                           q_rot=self.q, causal=self.causal, scale=self.scale, stream=stream)
 
     def backward(self, do, stream=None):
         _zero(stream, self.dq, self.dk, self.dv)
-        L.ea_attn_bwd(self.q, self.k, self.v, self.o, do, self.lse, self.delta, self.dq, self.dk, self.dv,
-                      self.q_seg, self.k_seg, self.causal, self.scale, delta_ready=False, stream=stream,
-                      workspace=self.panel)
-        if self.rope_theta is not None:
-            L.ea_rope(self.dq, self.dq, self.q_seg, self.rope_theta, inverse=True, stream=stream)
-            L.ea_rope(self.dk, self.dk, self.k_seg, self.rope_theta, inverse=True, stream=stream)
+        args = (self.q, self.k, self.v, self.o, do, self.lse, self.delta, self.dq, self.dk, self.dv, self.q_seg,
+                self.k_seg)
+        if self.rope_theta is None:
+            L.ea_attn_bwd(*args, self.causal, self.scale, delta_ready=False, stream=stream)
+        else:
+            L.ea_attn_bwd_rope(*args, self.rope_theta, self.causal, self.scale, delta_ready=False, stream=stream)
 
     def step(self, do, stream=None):
         self.forward(stream)
@@ -176,11 +164,9 @@ class ZigzagRingRank:
     fused_merge: steps after the first merge their partial result into (o, lse)
            inside the forward launch (``ea_attn_fwd_merge``); False writes each
            partial to its own buffers and merges it with ``ea_lse_merge``.
-    panel_bytes: as for DenseCausal; one workspace serves every ring step (the
-           steps run in order on one stream).
     """
 
-    def __init__(self, q, k, v, world, rank, scale=None, rope_theta=None, fused_merge=True, panel_bytes=None):
+    def __init__(self, q, k, v, world, rank, scale=None, rope_theta=None, fused_merge=True):
         B, sq, H, D = q.shape
         if sq % 2 or k.shape[1] != world * sq:
             raise ValueError("q must hold 2C rows and k/v W*2C rows")
@@ -210,48 +196,52 @@ class ZigzagRingRank:
         self.sources = [L.ea_ring_source(rank, t, world) for t in range(world)]
         self.k_segs = [L.ea_zigzag_segments(self.s_total, world, s) for s in self.sources]
         self.share_segs = [L.ea_zigzag_segments(self.s_total, world, s) for s in range(world)]
-        per_head = max(L.ea_attn_bwd_ws_bytes(sq, sq, self.q_seg, ks, True) for ks in self.k_segs)
-        self.panel = _panel(dev, per_head, B * H, panel_bytes)
 
     def _share(self, s, x):
         return x[:, 2 * self.C * s: 2 * self.C * (s + 1)]
-
-    def _rope_all(self, src_q, dst_q, src_k, dst_k, inverse, stream):
-        # each rank's share carries that rank's zigzag positions
-        L.ea_rope(src_q, dst_q, self.q_seg, self.rope_theta, inverse=inverse, stream=stream)
-        for s in range(self.W):
-            L.ea_rope(self._share(s, src_k), self._share(s, dst_k), self.share_segs[s], self.rope_theta,
-                      inverse=inverse, stream=stream)
 
     def _block(self, t, x):
         s = self.sources[t]
         return x[:, 2 * self.C * s: 2 * self.C * (s + 1)]
 
+    def _fwd(self, t, kb, vb, o, lse, merge, stream):
+        """One ring step's forward: a partial into (o, lse), or merged into that accumulator."""
+        if self.rope_theta is not None:
+            # q turned in the kernel; the turned rows are written once, at the first step
+            L.ea_attn_fwd_rope(self.q_in, kb, vb, o, lse, self.q_seg, self.k_segs[t], self.rope_theta,
+                               q_rot=self.q if t == 0 else None, merge=merge, causal=True, scale=self.scale,
+                               stream=stream)
+        elif merge:
+            L.ea_attn_fwd_merge(self.q, kb, vb, o, lse, self.q_seg, self.k_segs[t], True, self.scale, stream)
+        else:
+            L.ea_attn_fwd(self.q, kb, vb, o, lse, self.q_seg, self.k_segs[t], True, self.scale, stream)
+
     def forward(self, stream=None):
         if self.rope_theta is not None:
-            self._rope_all(self.q_in, self.q, self.k_in, self.k, False, stream)
+            # each rank's share carries that rank's zigzag positions
+            for s in range(self.W):
+                L.ea_rope(self._share(s, self.k_in), self._share(s, self.k), self.share_segs[s], self.rope_theta,
+                          stream=stream)
         for t in range(self.W):
             kb, vb = self._block(t, self.k), self._block(t, self.v)
             if t == 0:
-                L.ea_attn_fwd(self.q, kb, vb, self.o, self.lse, self.q_seg, self.k_segs[t], True, self.scale,
-                              stream)
+                self._fwd(t, kb, vb, self.o, self.lse, False, stream)
             elif self.fused_merge:
-                L.ea_attn_fwd_merge(self.q, kb, vb, self.o, self.lse, self.q_seg, self.k_segs[t], True,
-                                    self.scale, stream)
+                self._fwd(t, kb, vb, self.o, self.lse, True, stream)
             else:
-                L.ea_attn_fwd(self.q, kb, vb, self.o_part, self.lse_part, self.q_seg, self.k_segs[t], True,
-                              self.scale, stream)
+                self._fwd(t, kb, vb, self.o_part, self.lse_part, False, stream)
                 L.ea_lse_merge(self.o, self.lse, self.o_part, self.lse_part, stream)
 
     def backward(self, do, stream=None):
         _zero(stream, self.dq, self.dk, self.dv)
         for t in range(self.W):
             kb, vb = self._block(t, self.k), self._block(t, self.v)
-            L.ea_attn_bwd(self.q, kb, vb, self.o, do, self.lse, self.delta, self.dq, self._block(t, self.dk),
-                          self._block(t, self.dv), self.q_seg, self.k_segs[t], True, self.scale,
-                          delta_ready=(t > 0), stream=stream, workspace=self.panel)
-        if self.rope_theta is not None:
-            self._rope_all(self.dq, self.dq, self.dk, self.dk, True, stream)
+            args = (self.q, kb, vb, self.o, do, self.lse, self.delta, self.dq, self._block(t, self.dk),
+                    self._block(t, self.dv), self.q_seg, self.k_segs[t])
+            if self.rope_theta is None:
+                L.ea_attn_bwd(*args, True, self.scale, delta_ready=(t > 0), stream=stream)
+            else:
+                L.ea_attn_bwd_rope(*args, self.rope_theta, True, self.scale, delta_ready=(t > 0), stream=stream)
 
     def step(self, do, stream=None):
         self.forward(stream)

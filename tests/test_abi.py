@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
-    assert ea.ea_version() >= 100
+    assert ea.ea_version() >= 200
     assert ea.strerror(OK) == "ok"
 
 
@@ -221,6 +221,76 @@ def test_python_binding_rejects_bad_views():
         ea.ea_attn_fwd(q.transpose(1, 2), q, q, o, lse, [0, 8], [0, 8])
 
 
+def _bf(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def _f32(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.float32)
+
+
+def _expect(match, fn, *args, **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(*args, **kw)
+
+
+def test_python_binding_checks_before_the_library():
+    """Every wrapper checks dtypes, the B/Sq/Sk extents, strides and the device of every tensor first: a wrong
+    tensor would otherwise reach the kernels (a host pointer, a batch past the end, fp32 writes into bf16)."""
+    B, S, Sk, H, D = 2, 8, 6, 2, 64
+    q, do, k, v = _bf(B, S, H, D), _bf(B, S, H, D), _bf(B, Sk, H, D), _bf(B, Sk, H, D)
+    o, dq, dk, dv = _f32(B, S, H, D), _f32(B, S, H, D), _f32(B, Sk, H, D), _f32(B, Sk, H, D)
+    lse, delta = _f32(B, S, H), _f32(B, S, H)
+    seg_q, seg_k = [0, S], [0, Sk]
+    fwd = lambda **c: ea.ea_attn_fwd(**{**dict(q=q, k=k, v=v, o=o, lse=lse, q_seg=seg_q, k_seg=seg_k), **c})
+    bwd = lambda **c: ea.ea_attn_bwd(**{**dict(q=q, k=k, v=v, o=o, dout=do, lse=lse, delta=delta, dq=dq, dk=dk,
+                                               dv=dv, q_seg=seg_q, k_seg=seg_k), **c})
+    # batch count: k with one batch against q's two would read past the end of k
+    _expect("k must be", fwd, k=_bf(1, Sk, H, D), v=_bf(1, Sk, H, D))
+    _expect("v must have shape", fwd, v=_bf(B, Sk + 1, H, D))
+    _expect("o must have shape", fwd, o=_f32(B, S + 1, H, D))
+    _expect("lse must have shape", fwd, lse=_f32(1, S, H))
+    _expect("lse must be", fwd, lse=_bf(B, S, H))
+    # fp32 outputs: a bf16 buffer would take writes up to twice its size
+    for name, bad in (("dq", _bf(B, S, H, D)), ("dk", _bf(B, Sk, H, D)), ("dv", _bf(B, Sk, H, D)),
+                      ("delta", _bf(B, S, H)), ("lse", _bf(B, S, H))):
+        _expect(f"{name} must be torch.float32", bwd, **{name: bad})
+    _expect("dout must have shape", bwd, dout=_bf(B, Sk, H, D))
+    _expect("dk must have shape", bwd, dk=_f32(B, S, H, D))
+    _expect("delta must have shape", bwd, delta=_f32(B, S + 2, H))
+    _expect("q must be", bwd, q=_f32(B, S, H, D))
+    _expect("o is needed", bwd, o=None)
+    # the merge: fp32 accumulators, matching shapes
+    _expect("o_acc must be", ea.ea_lse_merge, _bf(B, S, H, D), lse, o, lse)
+    _expect("lse_part must be", ea.ea_lse_merge, o, lse, o, _bf(B, S, H))
+    _expect("o_part must have shape", ea.ea_lse_merge, o, lse, _f32(B, S - 1, H, D), lse)
+    _expect("lse_acc must have shape", ea.ea_lse_merge, o, _f32(B, S - 1, H), o, lse)
+    # the fused-merge forward needs an fp32 accumulator; the rotary forward a bf16 q_rot of q's shape
+    _expect("o must be torch.float32", ea.ea_attn_fwd_merge, q, k, v, _bf(B, S, H, D), lse, seg_q, seg_k)
+    _expect("q_rot must be", ea.ea_attn_fwd_rope, q, k, v, o, lse, seg_q, seg_k, 1e6, q_rot=o)
+    _expect("q_rot must have shape", ea.ea_attn_fwd_rope, q, k, v, o, lse, seg_q, seg_k, 1e6, q_rot=_bf(B, S, H + 1, D))
+    _expect("o must be torch.float32", ea.ea_attn_fwd_rope, q, k, v, _bf(B, S, H, D), lse, seg_q, seg_k, 1e6,
+            merge=True)
+    _expect("x must be", ea.ea_rope, torch_int(B, S, H, D), torch_int(B, S, H, D), seg_q, 1e6)
+    # every check above passes for these host tensors, so the device check is what stops them
+    _expect("on cpu", fwd)
+    _expect("on cpu", bwd)
+    _expect("on cpu", ea.ea_attn_fwd_rope, q, k, v, o, lse, seg_q, seg_k, 1e6, q_rot=_bf(B, S, H, D))
+    _expect("on cpu", ea.ea_attn_bwd_rope, q, k, v, o, do, lse, delta, dq, dk, dv, seg_q, seg_k, 1e6)
+    _expect("on cpu", ea.ea_lse_merge, o, lse, _bf(B, S, H, D), lse)
+    _expect("on cpu", ea.ea_rope, q, q, seg_q, 1e6)
+    import torch
+    x, y = _bf(4, 16), torch.zeros(4, dtype=torch.int64)
+    _expect("on cpu", ea.ea_xent_fwd_bwd, x, y, _f32(4), _f32(4))
+
+
+def torch_int(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.int32)
+
+
 def _rope(**kw):
     a = dict(x=P, y=P + STEP, dt=1, B=1, H=32, S=1024, D=128, br=1024, seg=(0, 1024), theta=1e6, inv=0)
     a.update(kw)
@@ -249,92 +319,85 @@ def test_rope_empty_is_noop():
     assert _rope(S=0, br=0, seg=(5, 0), x=0, y=0) == OK
 
 
-# ---- backward with the dS panel in a caller workspace (ea_attn_bwd_ws, ea_attn_bwd_ws_bytes)
-WORKSPACE = 8
+# ---- forward and backward with the rotary embedding fused in (ea_attn_fwd_rope, ea_attn_bwd_rope)
 
-
-def _panel_blocks_brute(pos_q, pos_k, causal):
-    """(256-query block, 32-key group) pairs holding at least one allowed pair, counted over positions."""
-    n = 0
-    for i0 in range(0, len(pos_q), 256):
-        qmax = pos_q[i0:i0 + 256].max()
-        for j0 in range(0, len(pos_k), 32):
-            if not causal or pos_k[j0:j0 + 32].min() <= qmax:
-                n += 1
-    return n
-
-
-@pytest.mark.parametrize("sq,sk,q_seg,k_seg,causal", [
-    (512, 512, [0, 512], [0, 512], True),
-    (1000, 1000, [0, 1000], [0, 1000], True),
-    (333, 200, [0, 333], [0, 200], False),
-    (777, 1301, [300, 400, 2000, 377], [0, 650, 1800, 651], True),
-    (190, 190, [0, 190], [100, 190], True),
-    (300, 400, [2 ** 31 - 300, 300], [2 ** 31 - 500, 400], True),
-    (200, 200, [2 ** 31 - 200, 100, 1000, 100], [2 ** 31 - 150, 150, 0, 50], True),
-    (1, 450, [449, 1], [0, 450], True),
-    (450, 1, [0, 450], [5000, 1], True),  # no allowed pair at all
-])
-def test_panel_bytes_match_brute_force(sq, sk, q_seg, k_seg, causal):
-    from tests.parity import seg_positions
-    got = ea.ea_attn_bwd_ws_bytes(sq, sk, q_seg, k_seg, causal)
-    assert got == _panel_blocks_brute(seg_positions(q_seg), seg_positions(k_seg), causal) * 256 * 32 * 2
-
-
-@pytest.mark.parametrize("W,C", [(8, 37), (4, 100), (8, 43750 // 16)])
-def test_panel_bytes_zigzag_steps(W, C):
-    for r in (0, W // 2, W - 1):
-        pq = oracle.zigzag_positions(2 * W * C, W, r)
-        for t in range(W):
-            s = oracle.ring_source(r, t, W)
-            pk = oracle.zigzag_positions(2 * W * C, W, s)
-            got = ea.ea_attn_bwd_ws_bytes(2 * C, 2 * C, ea.ea_zigzag_segments(2 * W * C, W, r),
-                                          ea.ea_zigzag_segments(2 * W * C, W, s), True)
-            assert got == _panel_blocks_brute(pq, pk, True) * 16384, (r, t)
-
-
-def test_panel_bytes_errors():
-    out = ctypes.c_int64(-1)
-    qs, nq = _seg(0, 100)
-    ks, nk = _seg(0, 50)
-    lib = ea.lib()
-    assert lib.ea_attn_bwd_ws_bytes(100, 50, qs, nq, ks, nk, 1, None) == NULL
-    assert lib.ea_attn_bwd_ws_bytes(100, 60, qs, nq, ks, nk, 1, ctypes.byref(out)) == POS
-    assert lib.ea_attn_bwd_ws_bytes(100, 50, qs, nq, ks, nk, 3, ctypes.byref(out)) == UNSUP
-    assert lib.ea_attn_bwd_ws_bytes(-1, 50, qs, nq, ks, nk, 1, ctypes.byref(out)) == SHAPE
-    z, nz = _seg(0, 0)
-    assert lib.ea_attn_bwd_ws_bytes(0, 50, z, nz, ks, nk, 1, ctypes.byref(out)) == OK and out.value == 0
-
-
-WS = P + 10 * STEP
-
-
-def _bwd_ws(ws=WS, ws_bytes=1 << 30, **kw):
-    a = dict(q=P, k=P + STEP, v=P + 2 * STEP, o=P + 3 * STEP, o_dtype=0, do=P + 4 * STEP, lse=P + 5 * STEP,
-             delta=P + 6 * STEP, ready=0, dq=P + 7 * STEP, dk=P + 8 * STEP, dv=P + 9 * STEP, B=1, H=2, Sq=128,
-             Sk=256, D=64, qbr=128, kbr=256, qseg=(0, 128), kseg=(0, 256), mask=1, scale=0.125)
+def _fwd_rope(**kw):
+    a = dict(q=P, k=P + STEP, v=P + 2 * STEP, o=P + 3 * STEP, o_dtype=0, lse=P + 4 * STEP, qr=P + 5 * STEP, merge=0,
+             B=1, H=2, Sq=128, Sk=128, D=128, qbr=128, kbr=128, qseg=(0, 128), kseg=(0, 128), mask=1, scale=0.088,
+             theta=1e6)
     a.update(kw)
     qs, nq = _seg(*a["qseg"])
     ks, nk = _seg(*a["kseg"])
     vp = ctypes.c_void_p
-    return ea.lib().ea_attn_bwd_ws(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), a["o_dtype"], vp(a["do"]),
-                                   vp(a["lse"]), vp(a["delta"]), a["ready"], vp(a["dq"]), vp(a["dk"]),
-                                   vp(a["dv"]), a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["qbr"], a["kbr"], qs,
-                                   nq, ks, nk, a["mask"], a["scale"], vp(ws), ws_bytes, None)
+    return ea.lib().ea_attn_fwd_rope(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), a["o_dtype"], vp(a["lse"]),
+                                     vp(a["qr"]), a["merge"], a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["qbr"],
+                                     a["kbr"], qs, nq, ks, nk, a["mask"], a["scale"], a["theta"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(ws_bytes=16384 * 4 - 16), WORKSPACE),   # one (batch, head) needs 4 blocks here (keys 0..127)
-    (dict(ws_bytes=0), WORKSPACE),
-    (dict(ws=0), NULL),
-    (dict(ws=WS + 8), ALIGN),
-    (dict(ws=P + 7 * STEP - 4096), ALIAS),          # runs into dq
-    (dict(ws=P + 2 * STEP), ALIAS),                 # over v
-    (dict(q=0), NULL), (dict(D=32), UNSUP), (dict(kseg=(0, 255)), POS), (dict(dq=P), ALIAS),
+    (dict(q=0), NULL), (dict(o=0), NULL), (dict(lse=0), NULL), (dict(k=0), NULL),
+    (dict(B=0), SHAPE), (dict(D=96), UNSUP), (dict(mask=2), UNSUP), (dict(scale=0.0), UNSUP),
+    (dict(theta=0.0), UNSUP), (dict(theta=-1e4), UNSUP), (dict(theta=float("inf")), UNSUP),
+    (dict(theta=float("nan")), UNSUP), (dict(merge=2), UNSUP), (dict(merge=-1), UNSUP),
+    (dict(merge=1, o_dtype=1), UNSUP), (dict(qseg=(0, 100)), POS),
+    (dict(qr=P + 5 * STEP + 8), ALIGN), (dict(q=P + 8), ALIGN),
+    (dict(qr=P), ALIAS), (dict(qr=P + 3 * STEP + 64), ALIAS), (dict(qr=P + STEP), ALIAS), (dict(o=P), ALIAS),
 ])
-def test_bwd_ws_rejects_bad_arguments(kw, code):
-    assert _bwd_ws(**kw) == code
+def test_fwd_rope_rejects_bad_arguments(kw, code):
+    assert _fwd_rope(**kw) == code
 
 
-def test_bwd_ws_empty_query_is_a_noop():
-    assert _bwd_ws(Sq=0, qseg=(0, 0), q=0, ws=0, ws_bytes=0) == OK
+def test_fwd_rope_empty_query_is_a_noop_without_pointers():
+    assert _fwd_rope(Sq=0, qseg=(0, 0), q=0, o=0, lse=0, qr=0) == OK
+
+
+def _bwd_rope(**kw):
+    a = dict(q=P, k=P + STEP, v=P + 2 * STEP, o=P + 3 * STEP, o_dtype=0, do=P + 4 * STEP, lse=P + 5 * STEP,
+             delta=P + 6 * STEP, ready=0, dq=P + 7 * STEP, dk=P + 8 * STEP, dv=P + 9 * STEP, B=1, H=2, Sq=128,
+             Sk=256, D=64, qbr=128, kbr=256, qseg=(0, 128), kseg=(0, 256), mask=1, scale=0.125, theta=1e9)
+    a.update(kw)
+    qs, nq = _seg(*a["qseg"])
+    ks, nk = _seg(*a["kseg"])
+    vp = ctypes.c_void_p
+    return ea.lib().ea_attn_bwd_rope(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), a["o_dtype"], vp(a["do"]),
+                                     vp(a["lse"]), vp(a["delta"]), a["ready"], vp(a["dq"]), vp(a["dk"]),
+                                     vp(a["dv"]), a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["qbr"], a["kbr"], qs,
+                                     nq, ks, nk, a["mask"], a["scale"], a["theta"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), NULL), (dict(dq=0), NULL), (dict(dk=0), NULL), (dict(o=0), NULL),
+    (dict(theta=0.0), UNSUP), (dict(theta=float("inf")), UNSUP), (dict(theta=float("nan")), UNSUP),
+    (dict(D=32), UNSUP), (dict(H=0), SHAPE), (dict(kseg=(0, 255)), POS),
+    (dict(dq=P + 7 * STEP + 4), ALIGN), (dict(dq=P), ALIAS), (dict(dk=P + 5 * STEP), ALIAS),
+])
+def test_bwd_rope_rejects_bad_arguments(kw, code):
+    assert _bwd_rope(**kw) == code
+
+
+def test_bwd_rope_empty_query_is_a_noop():
+    assert _bwd_rope(Sq=0, qseg=(0, 0), q=0, do=0, lse=0, delta=0, dq=0, o=0) == OK
+
+
+# ---- launch sizes: a grid needing 2^32 threads or more is a shape error found on the host.  The cases just
+# below each bound carry a misaligned pointer, an error checked after the sizes, so no call ever launches.
+
+def test_attention_launch_size_bounds():
+    # Delta: B*H*Sq*D/8 threads in 256-thread workgroups
+    assert _fwd(H=1024, Sq=1 << 18, qbr=1 << 18, qseg=(0, 1 << 18), q=P + 8) == SHAPE
+    assert _fwd(H=1024, Sq=(1 << 18) - 16, qbr=(1 << 18) - 16, qseg=(0, (1 << 18) - 16), q=P + 8) == ALIGN
+    assert _bwd(H=2048, D=64, Sq=1 << 18, qbr=1 << 18, qseg=(0, 1 << 18), dq=P + 7 * STEP + 4) == SHAPE
+    # dK/dV: B*H*ceil(Sk/128) workgroups of 512 threads
+    big = 1 << 20
+    assert _bwd(H=1024, Sk=big, kbr=big, kseg=(0, big), dq=P + 7 * STEP + 4) == SHAPE
+    assert _bwd(H=1024, Sk=big - 128, kbr=big - 128, kseg=(0, big - 128), dq=P + 7 * STEP + 4) == ALIGN
+    assert _fwd_rope(H=1024, Sq=1 << 18, qbr=1 << 18, qseg=(0, 1 << 18), q=P + 8) == SHAPE
+
+
+def test_elementwise_launch_size_bounds():
+    assert _merge(H=1024, D=128, Sq=1 << 18, qbr=1 << 18) == SHAPE
+    assert _merge(H=1024, D=128, Sq=(1 << 18) - 16, qbr=(1 << 18) - 16, oa=P + 4) == ALIGN
+    assert _xent(rows=1 << 23) == SHAPE
+    assert _xent(rows=(1 << 23) - 1, y=P + STEP + 4) == ALIGN
+    assert _rope(B=1, S=1 << 26, br=1 << 26, seg=(0, 1 << 26)) == SHAPE
+    assert _rope(B=1, S=(1 << 26) - 4, br=(1 << 26) - 4, seg=(0, (1 << 26) - 4), x=P + 8) == ALIGN

@@ -1,5 +1,5 @@
-"""A whole step recorded as a HIP graph (``capture_step``) against the same step run eagerly, on both backward
-paths (dQ by recomputation, and dQ from the dS panel in a workspace, also in head groups).
+"""A whole step recorded as a HIP graph (``capture_step``) against the same step run eagerly, with and without
+the rotary embedding fused into the attention calls, dense and ring.
 
 Each replay follows eager work of the program's own (an eager step of a second driver on the same inputs, and
 new inputs copied in place) with synchronisations in between, and every replay must reproduce the eager results
@@ -39,26 +39,19 @@ def _replays_match(make, inputs, reseed, n=3):
             assert torch.equal(getattr(drv, name), getattr(ref, name)), (i, name)
 
 
-@pytest.mark.parametrize("rope,panel", [(None, None), (1e6, None), (None, 1 << 40)])
-def test_dense_step_graph(rope, panel):
+@pytest.mark.parametrize("rope", [None, 1e6])
+def test_dense_step_graph(rope):
     B, S, H, D = 1, 700, 4, 128
-    banner(f"graph DenseCausal S={S} H={H} rope={rope} panel={panel}")
+    banner(f"graph DenseCausal S={S} H={H} rope={rope}")
     inputs = {n: _draw((B, S, H, D), 300 + i) for i, n in enumerate(("q", "k", "v", "do"))}
-    _replays_match(lambda: ea.DenseCausal(inputs["q"], inputs["k"], inputs["v"], rope_theta=rope,
-                                          panel_bytes=panel), inputs, 400)
+    _replays_match(lambda: ea.DenseCausal(inputs["q"], inputs["k"], inputs["v"], rope_theta=rope), inputs, 400)
 
 
-@pytest.mark.parametrize("one_head_panel", [False, True])
-def test_ring_step_graph(one_head_panel):
-    """The ring rank's step; with a workspace for one head's dS panel, every backward step runs head groups."""
+@pytest.mark.parametrize("rope", [None, 1e6])
+def test_ring_step_graph(rope):
     W, C, H, D, rank = 4, 40, 2, 64, 2
-    banner(f"graph ZigzagRingRank W={W} C={C} rank={rank} one_head_panel={one_head_panel}")
+    banner(f"graph ZigzagRingRank W={W} C={C} rank={rank} rope={rope}")
     inputs = {"q": _draw((1, 2 * C, H, D), 500), "k": _draw((1, 2 * W * C, H, D), 501),
               "v": _draw((1, 2 * W * C, H, D), 502), "do": _draw((1, 2 * C, H, D), 503)}
-    panel = None
-    if one_head_panel:
-        qs = ea.ea_zigzag_segments(2 * W * C, W, rank)
-        panel = max(ea.ea_attn_bwd_ws_bytes(2 * C, 2 * C, qs, ea.ea_zigzag_segments(2 * W * C, W, s), True)
-                    for s in range(W))
-    _replays_match(lambda: ea.ZigzagRingRank(inputs["q"], inputs["k"], inputs["v"], W, rank, rope_theta=1e6,
-                                             panel_bytes=panel), inputs, 600)
+    _replays_match(lambda: ea.ZigzagRingRank(inputs["q"], inputs["k"], inputs["v"], W, rank, rope_theta=rope),
+                   inputs, 600)

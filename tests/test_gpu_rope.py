@@ -131,3 +131,62 @@ def test_zigzag_ring_with_rope(rank):
     assert_close("dQ", drv.dq, ref["dq"])
     assert_close("dK", drv.dk, ref["dk"])
     assert_close("dV", drv.dv, ref["dv"])
+
+
+FUSED_CASES = [
+    # B, Sq, Sk, H, D, q_seg, k_seg, theta, causal
+    (1, 300, 300, 2, 128, [0, 300], [0, 300], 1e6, True),
+    (2, 257, 190, 3, 64, [5000, 257], [4900, 190], 1e4, True),
+    (1, 200, 260, 2, 128, [2 ** 31 - 300, 100, 70000, 100], [2 ** 31 - 400, 130, 69990, 130], 1e9, True),
+    (1, 96, 64, 1, 128, [640, 96], [0, 64], 1e6, False),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[f"fused{i}" for i in range(len(FUSED_CASES))])
+def test_fused_rope_matches_separate_rotation(case):
+    """ea_attn_fwd_rope / ea_attn_bwd_rope against ea_rope around ea_attn_fwd / ea_attn_bwd on the same inputs.
+
+    The forward turns q with the same arithmetic as ea_rope, so q_rot, O and LSE must agree bit for bit (also
+    merged into an accumulator).  The backward turns dQ, dK before adding them instead of after: dV and Delta are
+    bit-identical, dQ and dK agree to fp32 rounding (1e-6 of the pair length), also after a second accumulating
+    call."""
+    B, sq, sk, H, D, qs, ks, theta, causal = case
+    banner(f"fused rope B={B} Sq={sq} Sk={sk} H={H} D={D} q_seg={qs} k_seg={ks} theta={theta:g} causal={causal}")
+    draw = lambda shape, seed: synth.normal_draw(shape, seed, 1.0, DEV).to(torch.bfloat16)
+    q, do = draw((B, sq, H, D), 21), draw((B, sq, H, D), 22)
+    k, v = draw((B, sk, H, D), 23), draw((B, sk, H, D), 24)
+    qr, kr = torch.empty_like(q), torch.empty_like(k)
+    ea.ea_rope(q, qr, qs, theta)
+    ea.ea_rope(k, kr, ks, theta)
+    f32 = lambda *s: torch.zeros(*s, device=DEV)
+    o1, lse1, o2, lse2 = f32(B, sq, H, D), f32(B, sq, H), f32(B, sq, H, D), f32(B, sq, H)
+    q_rot = torch.full_like(q, float("nan"))
+    ea.ea_attn_fwd(qr, kr, v, o1, lse1, qs, ks, causal)
+    ea.ea_attn_fwd_rope(q, kr, v, o2, lse2, qs, ks, theta, q_rot=q_rot, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(q_rot, qr), "q_rot differs from ea_rope"
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2), "fused forward differs from rotate-then-forward"
+    # merged into an accumulator holding the first result: both paths again bit for bit
+    ea.ea_attn_fwd_merge(qr, kr, v, o1, lse1, qs, ks, causal)
+    ea.ea_attn_fwd_rope(q, kr, v, o2, lse2, qs, ks, theta, merge=True, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2), "fused merging forward differs"
+    # backward from the first forward's statistics
+    ea.ea_attn_fwd(qr, kr, v, o1, lse1, qs, ks, causal)
+    grads = [[f32(B, sq, H, D), f32(B, sk, H, D), f32(B, sk, H, D), f32(B, sq, H)] for _ in range(2)]
+    for calls in (1, 2):
+        for _ in range(calls if calls == 1 else 1):
+            ea.ea_attn_bwd(qr, kr, v, o1, do, lse1, grads[0][3], grads[0][0], grads[0][1], grads[0][2], qs, ks,
+                           causal)
+            ea.ea_attn_bwd_rope(qr, kr, v, o1, do, lse1, grads[1][3], grads[1][0], grads[1][1], grads[1][2], qs, ks,
+                                theta, causal)
+        dq_sep, dk_sep = grads[0][0].clone(), grads[0][1].clone()
+        ea.ea_rope(dq_sep, dq_sep, qs, theta, inverse=True)
+        ea.ea_rope(dk_sep, dk_sep, ks, theta, inverse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(grads[0][2], grads[1][2]) and torch.equal(grads[0][3], grads[1][3]), "dV or Delta differs"
+        for name, sep, fused in (("dQ", dq_sep, grads[1][0]), ("dK", dk_sep, grads[1][1])):
+            pair = torch.sqrt(sep[..., :D // 2] ** 2 + sep[..., D // 2:] ** 2).repeat(1, 1, 1, 2) + 1e-30
+            worst = float(((fused - sep).abs() / pair).max())
+            print(f"  {name} after {calls} call(s): max err / pair length {worst:.2e}", flush=True)
+            assert worst <= 1e-6, name
