@@ -327,17 +327,33 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   };
   // acc += (tile^T operand) x (the packs), two 16-query k-steps; the transposed
   // operand is dO (A: dV) or Q (B: dK) of the tile in stage STAGE
+  //
+  // The transposed operands go through a register ring two products deep (the
+  // reads of product i+2 are issued before product i), pinned by scheduling
+  // groups: left to itself the compiler read each operand right before its
+  // product and waited for it, so one wave spent an LDS latency per product.
   auto accumulate = [&](auto ROLE, int stage, const bf16x8* pk) {
     constexpr int base = decltype(ROLE)::value == 0 ? OT : 0;
+    constexpr int N = 2 * NDB, PF = 2;  // products (k-step major), read distance
+    auto rd = [&](int i) {
+      const int kk = i / NDB, db = i % NDB;
+      const u32x2 lo = ds_read_tr16(&QO[stage][base + tofs[0][db] + 16 * kk * D]);
+      const u32x2 hi = ds_read_tr16(&QO[stage][base + tofs[1][db] + 16 * kk * D]);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 fr[N];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int i = 0; i < PF; ++i) fr[i] = rd(i);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2 lo = ds_read_tr16(&QO[stage][base + tofs[0][db] + 16 * kk * D]);
-        const u32x2 hi = ds_read_tr16(&QO[stage][base + tofs[1][db] + 16 * kk * D]);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        acc[db] = mfma32(as_bf16x8(a), pk[kk], acc[db]);
-      }
+    for (int i = 0; i < N; ++i) {
+      if (i + PF < N) fr[i + PF] = rd(i + PF);
+      acc[i % NDB] = mfma32(as_bf16x8(fr[i]), pk[i / NDB], acc[i % NDB]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);  // the first PF products' reads
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // product i
+      if (i + PF < N) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of product i + PF
     }
   };
 
@@ -383,18 +399,43 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   // and dP(t-1) (in dp_cur); dK^T += Q(t-1)^T dS(t-1).  PSTAGE = stage of t-1.
   auto step_b = [&](int stage, int pstage, auto DO_DP, int t, f32x16& dp_cur, f32x16& dp_nx) {
     constexpr bool do_dp = decltype(DO_DP)::value;  // false: last step, no tile t
+    constexpr int PF = 2;                           // read distance of the dO operands
     const bool prev = t > 0;
     float dsv[16];
-    const float* psrc = &Ps[(t + 1) & 1][kw][0][lane][0];
+    // P(t-1) and Delta of the 16 queries this lane holds, four at a time (Ps[slot][kw][m][lane][0..3] and
+    // Ss[pstage][BQ + 8m + 4g + 0..3]), each group loaded one group ahead of its use
+    const f32x4* psrc4 = reinterpret_cast<const f32x4*>(&Ps[(t + 1) & 1][kw][0][lane][0]);
+    const f32x4* dsrc4 = reinterpret_cast<const f32x4*>(&Ss[pstage][BQ + 4 * g]);
+    auto rd = [&](int ks) {
+      return *reinterpret_cast<const u32x4*>(&QO[stage][qbase + ((ks ^ qx) << 4) + OT]);
+    };
+    u32x4 fr[NKS];
+    if constexpr (do_dp) {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) fr[i] = rd(i);
+    }
+    f32x4 pm[4], dm[4];
+    pm[0] = psrc4[0];
+    dm[0] = dsrc4[0];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      if constexpr (do_dp) score_k(RB{}, stage, ks, dp_nx);
+      if constexpr (do_dp) {
+        if (ks + PF < NKS) fr[ks + PF] = rd(ks + PF);
+        dp_nx = mfma32(as_bf16x8(fr[ks]), kvf[ks], ks == 0 ? f32x16{} : dp_nx);
+      }
+      constexpr int GS = NKS / 4;  // k-steps per group of four values (two at D = 128, one at D = 64)
+      if (ks % GS == 0) {
+        const int m = ks / GS;
+        if (m + 1 < 4) {
+          pm[m + 1] = psrc4[(m + 1) * 64];
+          dm[m + 1] = dsrc4[2 * (m + 1)];
+        }
 #pragma unroll
-      for (int u = 0; u < 16 / NKS; ++u) {
-        const int r = (16 / NKS) * ks + u;
-        const float pr = psrc[(r >> 2) * 256 + (r & 3)];
-        const float ds = pr * (dp_cur[r] - Ss[pstage][BQ + 8 * (r >> 2) + 4 * g + (r & 3)]);
-        dsv[r] = prev ? ds : 0.f;  // step 0 has no tile t-1: add zeros (keeps the accumulation unconditional)
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * m + e;
+          const float ds = pm[m][e] * (dp_cur[r] - dm[m][e]);
+          dsv[r] = prev ? ds : 0.f;  // step 0 has no tile t-1: add zeros (keeps the accumulation unconditional)
+        }
       }
     }
     bf16x8 pk[2];
