@@ -131,9 +131,7 @@ __device__ __forceinline__ void rope_back(f32x16 (&acc)[NDB], int pos, const dou
 // P (software pipeline) and publishes P(t); B computes dP(t) while forming
 // dS(t-1) from P(t-1), published one step earlier, so the one workgroup barrier
 // per step orders both the ring and the exchange.  Each role runs its own copy
-// of the loop so that its accumulator stays in the same registers, and B runs at
-// issue priority 1 (its dP products open every step while A is still in the
-// exponentials).
+// of the loop so that its accumulator stays in the same registers.
 template <int D>
 struct DkdvCfg {
   static constexpr int NW = 8, NT = 512, BKV = 128, BQ = 32, NST = 6;
@@ -503,15 +501,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
         step_b(st, sp, std::false_type{}, nt, last, dummy);
       }
     };
-    if (role == 0) {
+    // both roles at the default issue priority: with the operand rings above, raising the V-side waves'
+    // priority (which helped when they waited on every operand) costs 2 %
+    if (role == 0)
       run(RA{});
-    } else {
-      // issue priority for the V-side waves: their dP products open each step
-      // while the K-side waves of the same SIMD are still in the exponentials
-      __builtin_amdgcn_s_setprio(1);
+    else
       run(RB{});
-      __builtin_amdgcn_s_setprio(0);
-    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // retire the trailing (unused) loads
   }
 
