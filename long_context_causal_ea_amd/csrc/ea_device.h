@@ -46,6 +46,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> fp16 of two values, packed low/high.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// Half `hi` (0: low, 1: high) of a packed fp16 pair, exactly as fp32.
+__device__ __forceinline__ float unpack_f16(uint32_t u, int hi) {
+  return (float)__builtin_bit_cast(f16x2, u)[hi];
+}
+
 __device__ __forceinline__ bf16x8 pack_bf16x8(float x0, float x1, float x2, float x3, float x4, float x5,
                                               float x6, float x7) {
   u32x4 u;
