@@ -125,10 +125,14 @@ __device__ __forceinline__ void rope_back(f32x16 (&acc)[NDB], int pos, const dou
 // the B-operand form of the dV / dK products; dO^T and Q^T are read from the
 // row-major tiles by the LDS transpose read.
 //
-// P crosses from A to B through LDS as fp16 pairs (round to nearest even; P is
-// in [0, 1], where fp16 keeps 11 significant bits against bf16's 8, and the
-// values it flushes to zero, below 6e-8, would add under 1e-6 to dS): half the
-// bytes of an fp32 hand-over, and the dK/dV pass 1 % faster.
+// P crosses from A to B through LDS as fp16 pairs (round to nearest even):
+// half the bytes of an fp32 hand-over.  Over long key ranges P is tiny (about
+// 1e-6 for a near-uniform row over 700K keys), below fp16's smallest normal
+// value, where only a few significant bits would survive; so both roles work
+// with P * 2^kPScaleLog2 (the exponent offset is folded into the base-2 LSE,
+// no extra arithmetic), which keeps every P >= 3.7e-9 normal in fp16 with 11
+// significant bits, and the epilogue multiplies the accumulators by the exact
+// inverse power of two.
 //
 // 32-row query tiles (Q, dO, LSE, Delta) stream through a 6-stage LDS ring of
 // direct global->LDS loads (tiles t-1 .. t+1 in use, t+2 .. t+4 in flight).  In
@@ -137,6 +141,9 @@ __device__ __forceinline__ void rope_back(f32x16 (&acc)[NDB], int pos, const dou
 // dS(t-1) from P(t-1), published one step earlier, so the one workgroup barrier
 // per step orders both the ring and the exchange.  Each role runs its own copy
 // of the loop so that its accumulator stays in the same registers.
+// The dK/dV pass works with P * 2^kPScaleLog2 (see the fp16 hand-over below).
+constexpr int kPScaleLog2 = 14;
+
 template <int D>
 struct DkdvCfg {
   static constexpr int NW = 8, NT = 512, BKV = 128, BQ = 32, NST = 6;
@@ -451,13 +458,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   };
 
   // Wave 0, which loads the per-row statistics, rewrites the LSE of a resident
-  // tile in base-2 units (-inf, a row without any allowed key, becomes +inf so
-  // that its recomputed probabilities are exactly 0); the next barrier
-  // publishes the converted values.
+  // tile in base-2 units less kPScaleLog2, so that exp2 gives 2^kPScaleLog2 P
+  // (-inf, a row without any allowed key, becomes +inf so that its recomputed
+  // probabilities are exactly 0); the next barrier publishes the converted
+  // values.
   auto to_log2 = [&](int stage) {
     if (w == 0 && g == 0) {
       const float l = Ss[stage][ln];
-      Ss[stage][ln] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
+      Ss[stage][ln] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e - kPScaleLog2;
     }
   };
 
@@ -523,7 +531,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   // (the rotation is linear, so turning each call's contribution before it is added is exact)
   if (role == 1 && p.rope) rope_back(acc, kpos, p.f, g);
   float* dst = (role == 0 ? p.dv : p.dk) + b * p.k_bstride + (long)h * D_ + (long)krow * p.rs;
-  const float mul = role == 0 ? 1.f : p.scale;
+  constexpr float kPUnscale = 1.f / (float)(1 << kPScaleLog2);  // exact: the accumulators hold 2^kPScaleLog2 P
+  const float mul = role == 0 ? kPUnscale : p.scale * kPUnscale;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
