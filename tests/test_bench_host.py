@@ -86,3 +86,19 @@ def test_rotary_bytes():
     b = bench.rope_bytes(65536, 32, 128)
     n = 65536 * 32 * 128
     assert b["fwd"] == 2 * n * 4 and b["inv"] == 2 * n * 8
+
+
+def test_compulsory_bytes_count_each_tensor_once():
+    """Per-launch minimum HBM bytes, tallied tensor by tensor at the 64K-token layer (B1 H32 D128, RoPE) and for a
+    ring step (C3: 2C = 65536 local rows and a 65536-key share per launch, 7 of 8 forwards merging)."""
+    n = 65536 * 32 * 128                 # elements of one [S, H, D] tensor
+    r = 65536 * 32                       # (row, head) pairs
+    bf16, f32 = 2 * n, 4 * n
+    t = synth.get("t")
+    assert bench.compulsory_bytes("fwd", t) == 3 * bf16 + f32 + 4 * r + bf16          # Q K V in, O LSE out, turned Q
+    assert bench.compulsory_bytes("bwd_dkdv", t) == 4 * bf16 + 2 * 4 * r + 2 * 2 * f32   # dK dV read and written
+    assert bench.compulsory_bytes("bwd_dq", t) == 4 * bf16 + 2 * 4 * r + 2 * f32
+    assert bench.compulsory_bytes("bwd_delta", t) == f32 + bf16 + 4 * r
+    c3 = synth.get("c3")
+    assert bench.compulsory_bytes("fwd", c3) == pytest.approx(3 * bf16 + f32 + 4 * r + (f32 + 4 * r) * 7 / 8)
+    assert bench.compulsory_bytes("bwd_dkdv", c3) == bench.compulsory_bytes("bwd_dkdv", t)
