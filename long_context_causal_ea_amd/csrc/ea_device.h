@@ -149,6 +149,14 @@ __device__ __forceinline__ void lds_ring_sync() {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// max(x of this lane, x of lane l ^ 32): gfx950's lane swap between the two
+// halves of a wave (a vector-ALU instruction, no LDS round trip).  Whichever
+// half each output holds, the larger of the two outputs is the pair's maximum.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Exponent base 2 on the hardware transcendental unit.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -6,12 +6,18 @@
 // gfx950 mapping
 //  - One workgroup = 8 waves = 256 query rows of one (batch, head), one
 //    workgroup (two waves per SIMD) per CU; each wave owns 32 rows.  Key/value
-//    tiles of 64 rows (two 32-key blocks) stream through a ring of LDS stages
-//    filled by direct global->LDS loads, three tiles in flight, so one barrier
-//    covers 32 matrix-core products per wave.
-//  - The loop is software-pipelined: each step first issues the scores of tile
-//    t+1 to the matrix cores, then runs the softmax of tile t (row maximum,
-//    rescale, exponentials) on the vector ALUs while they execute.
+//    tiles of 64 rows (two 32-key blocks) stream through a ring of 4 LDS stages
+//    filled by direct global->LDS loads, issued two tiles ahead.
+//  - Ping-pong between the two waves of each SIMD (waves w and w + 4): each
+//    tile takes a product phase (the scores of tile t and O += P V of tile t-1
+//    on the matrix cores) and a softmax phase (rescale, exponentials) on the
+//    vector ALU, and the two waves run them one phase apart, separated by
+//    workgroup barriers.  A wave that issues products and vector work in turn
+//    stalls its vector work behind every product that waits for the matrix
+//    core; in the ping-pong one wave feeds the matrix core while the other
+//    keeps the vector ALU busy.  The product phase also takes the row sums of
+//    the previous tile and the row maximum of the new scores, so the softmax
+//    phase is no longer than the product phase.
 //  - Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
 //    every lane then holds 32 scores of ONE query row, so the row max and row
 //    sum are in-lane reductions plus one exchange with lane l^32.
@@ -168,7 +174,11 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   // than 8 (in log2 units): probabilities then stay below 2^8, exactly
   // representable in the accumulation, and the rescale of O is rare.
   const float raise_thr = 8.f / p.c;
-  float m_run = NEG_INF, l_run = 0.f;
+  // The row sum is kept as four partial sums (summed at the end) and the row
+  // maximum of a tile is formed by four independent chains: a softmax phase
+  // runs alone on its SIMD's vector ALU, so its dependency chains are not
+  // hidden behind another wave's work.
+  float m_run = NEG_INF, l_run[4] = {0.f, 0.f, 0.f, 0.f};
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
@@ -233,117 +243,230 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
     return kmx <= qmin_w ? (int)kFull : (int)kPartial;
   };
 
-  // S^T = K Q^T of the tile in stage STAGE, one 32-key block per output;
-  // register r of block mb holds key 32*mb + 8*(r/4) + 4*g + r%4 of query ln
-  auto scores = [&](auto STAGE, f32x16 (&st)[NMB]) {
-    constexpr int stage = decltype(STAGE)::value;
+  // The compiler may move pure arithmetic across a barrier (it moved exponentials
+  // of a softmax phase into the next product phase, where their results are
+  // used); an empty asm statement that takes a phase's results as in-out
+  // operands keeps their computation before the phase's closing barrier.
+  auto pin_phase_outputs = [](f32x16 (&s16)[NMB], f32x16 (&o16)[NDB]) {
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      st[mb] = f32x16{};
+    for (int mb = 0; mb < NMB; ++mb) asm volatile("" : "+v"(s16[mb]));
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[stage][mb * 32 * D + kbase + ((ks ^ kx) << 4)]);
-        st[mb] = mfma32(as_bf16x8(a), qf[ks], st[mb]);
-      }
-    }
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(o16[db]));
+  };
+  f32x16 st[NMB];         // S^T of the tile between its product phase and its softmax phase
+  bf16x8 pb[2 * NMB];     // P^T as B operands, one per 16-key k-step, until the next product phase
+  float ep[16 * NMB];     // the same probabilities in fp32, added to the row sums in the next product phase
+  float mx_t = NEG_INF;   // row maximum of the tile's scores, formed in its product phase
+#pragma unroll
+  for (int kk = 0; kk < 2 * NMB; ++kk) pb[kk] = bf16x8{};
+#pragma unroll
+  for (int r = 0; r < 16 * NMB; ++r) ep[r] = 0.f;
+
+  // row maximum of st (both halves of the wave): four independent chains, then
+  // the lane swap
+  auto row_max = [&]() {
+    float m4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) m4[(r >> 1) & 3] = fmaxf(fmaxf(m4[(r >> 1) & 3], st[mb][r]), st[mb][r + 1]);
+    return xor32_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
   };
 
-  using I0 = std::integral_constant<int, 0>;
+  // Product phase of tile t: S^T(t) = K(t) Q^T from stage KSTAGE, then
+  // O^T += V^T(t-1) P^T(t-1) from stage VSTAGE (V^T read transposed from the
+  // row-major V tile).  No product waits for vector-ALU work.  The first phase
+  // (t = 0) adds P = 0 times the resident tile 0; the last (t = nt) computes the
+  // scores of the reloaded last tile and drops them, so every phase is the same
+  // straight run of products.  Their operands go through a register ring PF
+  // products deep, pinned by scheduling groups (left to itself the compiler read
+  // each K operand right before its product and waited for it).  Between the
+  // products the wave adds the previous tile's probabilities to its row sums and,
+  // once the scores have landed, forms their row maximum: vector work that
+  // would otherwise lengthen the softmax phase, which runs alone on its vector ALU.
+  auto m_phase = [&](auto KSTAGE, auto VSTAGE) {
+    constexpr int kstage = decltype(KSTAGE)::value, vstage = decltype(VSTAGE)::value;
+    constexpr int NS = NKS * NMB, NPV = 2 * NMB * NDB, N = NS + NPV, PF = 3;
+    constexpr int ADD_PER = (16 * NMB + NS - 1) / NS;     // row-sum adds per score product
+    constexpr int MAX_PER = (24 + NPV - 3) / (NPV - 2);  // row-maximum work per O product (after the first two)
+    static_assert(PF <= NS, "the ring starts inside the score products");
+    auto rd = [&](int i) {
+      if (i < NS) {  // K operand of score product i (k-step major)
+        const int ks = i / NMB, mb = i % NMB;
+        return *reinterpret_cast<const u32x4*>(&Ks[kstage][mb * 32 * D + kbase + ((ks ^ kx) << 4)]);
+      }
+      const int kk = (i - NS) / NDB, db = (i - NS) % NDB;  // V^T operand of O product i - NS
+      const u32x2 lo = ds_read_tr16(&Vs[vstage][vofs[0][db] + 16 * kk * D]);
+      const u32x2 hi = ds_read_tr16(&Vs[vstage][vofs[1][db] + 16 * kk * D]);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 fr[N];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) fr[i] = rd(i);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) st[mb] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + PF < N) fr[i + PF] = rd(i + PF);
+      if (i < NS) {
+        st[i % NMB] = mfma32(as_bf16x8(fr[i]), qf[i / NMB], st[i % NMB]);
+      } else {
+        const int j = i - NS;
+        oacc[j % NDB] = mfma32(as_bf16x8(fr[i]), pb[j / NDB], oacc[j % NDB]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16 * NMB; ++r) l_run[r & 3] += ep[r];
+    mx_t = row_max();
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // operands of the first PF products
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // product i
+      if (i + PF < NS) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the read of score product i + PF
+      } else if (i + PF < N) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two reads of O product i + PF - NS
+      }
+      if (i < NS) {
+        __builtin_amdgcn_sched_group_barrier(0x002, ADD_PER, 0);  // row-sum adds
+      } else if (i >= NS + 2) {
+        __builtin_amdgcn_sched_group_barrier(0x002, MAX_PER, 0);  // row maximum of the new scores
+      }
+    }
+    pin_phase_outputs(st, oacc);
+    asm volatile("" : "+v"(mx_t), "+v"(l_run[0]), "+v"(l_run[1]), "+v"(l_run[2]), "+v"(l_run[3]));
+  };
 
-  // one pipeline step: the scores of tile t+1 (into st_next, stage STAGE+1), then
-  // the softmax and P V of tile t (scores in st_cur, stage STAGE)
-  auto step = [&](auto STAGE, int t, f32x16 (&st_cur)[NMB], int& cls_cur, f32x16 (&st_next)[NMB], int& cls_next) {
-    constexpr int stage = decltype(STAGE)::value;
-    constexpr int nstage = (stage + 1) % NST, fstage = (stage + NST - 1) % NST;
-    // tile t+1 resident for every wave; everyone is done with stage (t-1) % NST
-    lds_ring_sync<(NST - 3) * LOADS_PER_TILE>();
-    issue_tile(std::integral_constant<int, fstage>{}, t + NST - 1);
+  // Softmax phase of tile t: mask (the maximum is then formed again), rescale,
+  // exponentials, P^T packed to bf16.
+  auto v_phase = [&](int t) {
     const int j0 = tile_of(t) * BK;
-    const bool has_next = t + 1 < nt;
-    cls_next = has_next ? classify(t + 1) : (int)kFull;
-
-    if (cls_cur == kPartial) {
+    float mx = mx_t;
+    if (classify(t) == kPartial) {
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = j0 + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-          st_cur[mb][r] = in_window(kwin, j) ? st_cur[mb][r] : NEG_INF;
+          st[mb][r] = in_window(kwin, j) ? st[mb][r] : NEG_INF;
         }
+      mx = row_max();
     }
-    // The scores of tile t+1 go to the matrix cores first: they do not depend on
-    // the softmax of tile t, so its maximum, rescale and exponentials (vector
-    // ALUs) run while they execute.  On the last tile the scores of a dummy tile
-    // are computed and dropped.
-    scores(std::integral_constant<int, nstage>{}, st_next);
-    float mx = NEG_INF;
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st_cur[mb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
     if (__any(mx > m_run + raise_thr)) {
       const float mnew = fmaxf(m_run, mx);
       const float alpha = (m_run == NEG_INF) ? 0.f : fast_exp2((m_run - mnew) * p.c);
-      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_run[i] *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
       m_run = mnew;
     }
-
     const float msub = (m_run == NEG_INF) ? 0.f : m_run * p.c;
-    bf16x8 pb[2 * NMB];  // P^T as B operands, one per 16-key k-step
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
-      float e[16];
+      float* e = ep + 16 * mb;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = fast_exp2(__builtin_fmaf(st_cur[mb][r], p.c, -msub));
-        l_run += e[r];
-      }
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(__builtin_fmaf(st[mb][r], p.c, -msub));
       pb[2 * mb] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       pb[2 * mb + 1] = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
     }
-    // O^T += V^T P^T; V^T read transposed from the row-major V tile.  Key steps outermost, so the first
-    // products need only the first packs of P (each accumulator still adds the key steps in order)
 #pragma unroll
-    for (int kk = 0; kk < 2 * NMB; ++kk)
+    for (int kk = 0; kk < 2 * NMB; ++kk) asm volatile("" : "+v"(pb[kk]));
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2 lo = ds_read_tr16(&Vs[stage][vofs[0][db] + 16 * kk * D]);
-        const u32x2 hi = ds_read_tr16(&Vs[stage][vofs[1][db] + 16 * kk * D]);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = mfma32(as_bf16x8(a), pb[kk], oacc[db]);
-      }
+    for (int r = 0; r < 16 * NMB; ++r) asm volatile("" : "+v"(ep[r]));
+    asm volatile("" : "+v"(l_run[0]), "+v"(l_run[1]), "+v"(l_run[2]), "+v"(l_run[3]), "+v"(m_run));
+    pin_phase_outputs(st, oacc);
+  };
+
+  // Phase boundaries.  Phase 2m starts once tile m is resident for every wave
+  // (each wave waits for its own loads of it, then the barrier), after which the
+  // load of tile m+2 goes out into the stage tile m-2 held: its last reader
+  // finished in phase 2m-1.  Odd phases start with a barrier alone.  The
+  // scheduling walls keep every instruction in its phase.
+  auto sync_even = [&](auto STAGE2, int m) {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_ring_sync<LOADS_PER_TILE>();
+    issue_tile(STAGE2, m + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto sync_odd = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   if (nt > 0) {
-    // prologue: NST-1 tiles in flight, scores of tile 0
-    static_assert(NST == 4, "the loop below is unrolled for a ring of 4 stages");
-    issue_tile(std::integral_constant<int, 0>{}, 0);
-    issue_tile(std::integral_constant<int, 1>{}, 1);
-    issue_tile(std::integral_constant<int, 2>{}, 2);
-    lds_ring_sync<(NST - 2) * LOADS_PER_TILE>();
-    int cls_a = classify(0), cls_b = kFull;
-    f32x16 st_a[NMB], st_b[NMB];
-    scores(I0{}, st_a);
-
-    // unrolled by the ring size so that every stage index is a constant and the
-    // two score buffers alternate without copies
-    for (int t = 0; t < nt; t += 4) {
-      step(std::integral_constant<int, 0>{}, t, st_a, cls_a, st_b, cls_b);
-      if (t + 1 >= nt) break;
-      step(std::integral_constant<int, 1>{}, t + 1, st_b, cls_b, st_a, cls_a);
-      if (t + 2 >= nt) break;
-      step(std::integral_constant<int, 2>{}, t + 2, st_a, cls_a, st_b, cls_b);
-      if (t + 3 >= nt) break;
-      step(std::integral_constant<int, 3>{}, t + 3, st_b, cls_b, st_a, cls_a);
+    static_assert(NST == 4, "the phase schedule below is written for a ring of 4 stages");
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    issue_tile(S0{}, 0);
+    issue_tile(S1{}, 1);
+    sync_even(S2{}, 0);
+    // Ping-pong: waves w and w + NW/2 share a SIMD.  The first half runs the
+    // product phase of tile t in phase 2t and the softmax of tile t in phase
+    // 2t+1; the second half runs one phase later.  So in every phase one wave of
+    // each SIMD issues only matrix-core products while the other runs only
+    // vector-ALU work, and the matrix cores never wait on a softmax.  Both halves
+    // pass the same 2*nt + 2 barriers.
+    if (w < Cfg::NW / 2) {
+      m_phase(S0{}, S0{});
+      for (int t0 = 0;; t0 += 4) {
+        sync_odd();
+        v_phase(t0);
+        sync_even(S3{}, t0 + 1);
+        m_phase(S1{}, S0{});
+        if (t0 + 1 == nt) break;
+        sync_odd();
+        v_phase(t0 + 1);
+        sync_even(S0{}, t0 + 2);
+        m_phase(S2{}, S1{});
+        if (t0 + 2 == nt) break;
+        sync_odd();
+        v_phase(t0 + 2);
+        sync_even(S1{}, t0 + 3);
+        m_phase(S3{}, S2{});
+        if (t0 + 3 == nt) break;
+        sync_odd();
+        v_phase(t0 + 3);
+        sync_even(S2{}, t0 + 4);
+        m_phase(S0{}, S3{});
+        if (t0 + 4 == nt) break;
+      }
+      sync_odd();
+    } else {
+      sync_odd();
+      m_phase(S0{}, S0{});
+      for (int t0 = 0;; t0 += 4) {
+        sync_even(S3{}, t0 + 1);
+        v_phase(t0);
+        sync_odd();
+        m_phase(S1{}, S0{});
+        if (t0 + 1 == nt) break;
+        sync_even(S0{}, t0 + 2);
+        v_phase(t0 + 1);
+        sync_odd();
+        m_phase(S2{}, S1{});
+        if (t0 + 2 == nt) break;
+        sync_even(S1{}, t0 + 3);
+        v_phase(t0 + 2);
+        sync_odd();
+        m_phase(S3{}, S2{});
+        if (t0 + 3 == nt) break;
+        sync_even(S2{}, t0 + 4);
+        v_phase(t0 + 3);
+        sync_odd();
+        m_phase(S0{}, S3{});
+        if (t0 + 4 == nt) break;
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // retire the trailing (unused) loads
   }
 
   // ---- epilogue: normalise, write O and LSE
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float l1 = (l_run[0] + l_run[1]) + (l_run[2] + l_run[3]);
+  const float lt = l1 + __shfl_xor(l1, 32);
   if (!row_ok) return;
   const bool has = lt > 0.f;
   const float inv = has ? 1.f / lt : 0.f;
