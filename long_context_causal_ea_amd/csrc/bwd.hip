@@ -17,7 +17,9 @@
 //             through a direct-to-LDS ring like the forward; recomputes S^T and
 //             dP^T with the query on the lane axis and accumulates
 //             dQ^T += K^T dS^T in registers (K^T by transpose read of the
-//             row-major K tile).
+//             row-major K tile).  Like the forward it runs a ping-pong between
+//             the two waves of each SIMD: product phases and arithmetic phases
+//             one phase apart, between workgroup barriers.
 // All LDS tiles are row-major with the XOR chunk swizzle of ea_device.h.
 // The dq pass recomputes the two score products instead of exchanging dS
 // through atomics (fp32 atomic adds into L2 were measured at about 1.4 TB/s on
@@ -550,12 +552,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 // SIMD, so each key/value tile in LDS serves eight waves; each wave owns
 // 32 rows and keeps their Q and dO rows as MFMA B operands and its dQ^T
 // accumulator in registers.  Key/value tiles of 32 rows stream through a
-// 4-stage direct-to-LDS ring (K and V of a stage side by side), three tiles in
-// flight, exactly like the forward.  Per tile: S^T = K Q^T and dP^T = V dO^T
-// (query on the lane axis, so each lane's LSE and Delta are one value), P and
-// dS = P (dP - Delta), then dQ^T += K^T dS^T with K^T read by the LDS transpose
-// read.  The score products of tile t+1 interleave with the P / dS arithmetic
-// of tile t.
+// 4-stage direct-to-LDS ring (K and V of a stage side by side), loaded two
+// tiles ahead, exactly like the forward.  Per tile: S^T = K Q^T and
+// dP^T = V dO^T (query on the lane axis, so each lane's LSE and Delta are one
+// value), P and dS = P (dP - Delta), then dQ^T += K^T dS^T with K^T read by the
+// LDS transpose read.  The products of tile t and the dQ product of tile t-1
+// form one phase, the P / dS arithmetic of tile t the next, and the two waves
+// of a SIMD run them one phase apart (the forward's ping-pong).
 template <int D>
 struct DqCfg {
   static constexpr int NW = 8, BQ = 32 * NW, BK = 32, NT = 64 * NW, NST = 4;
@@ -695,87 +698,171 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
     return kmx <= qmin_w ? (int)kFull : (int)kPartial;
   };
 
-  // S^T = K Q^T and dP^T = V dO^T of the tile in stage STAGE; register r of lane
-  // l holds key 8*(r/4) + 4*g + r%4 of query ln
-  auto score_k = [&](auto STAGE, int ks, f32x16& s, f32x16& dp) {
-    constexpr int stage = decltype(STAGE)::value;
-    const int o = kbase + ((ks ^ kx) << 4);
-    const u32x4 a = *reinterpret_cast<const u32x4*>(&KV[stage][o]);
-    s = mfma32(as_bf16x8(a), qf[ks], ks == 0 ? f32x16{} : s);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(&KV[stage][KT + o]);
-    dp = mfma32(as_bf16x8(v), of[ks], ks == 0 ? f32x16{} : dp);
-  };
-
   constexpr float NEG_INF = -__builtin_inff();
   const float c = p.c;
 
-  auto step = [&](auto STAGE, int t, f32x16& s_cur, f32x16& dp_cur, int& cls_cur, f32x16& s_nx, f32x16& dp_nx,
-                  int& cls_nx) {
-    constexpr int stage = decltype(STAGE)::value;
-    constexpr int nstage = (stage + 1) % NST, fstage = (stage + NST - 1) % NST;
-    lds_ring_sync<(NST - 3) * LOADS_PER_TILE>();  // tile t+1 resident; all done with stage (t-1) % NST
-    issue_tile(std::integral_constant<int, fstage>{}, t + NST - 1);
-    const int j0 = tile_of(t) * BK;
-    cls_nx = t + 1 < nt ? classify(t + 1) : (int)kFull;
-    if (cls_cur == kPartial) {
+  f32x16 sc, dpv;  // S^T and dP^T - Delta of a tile between its product phase and its arithmetic phase;
+                   // register r of lane l holds key 8*(r/4) + 4*g + r%4 of query ln
+  bf16x8 sb[2] = {bf16x8{}, bf16x8{}};  // dS^T of the previous tile, keys 0-15 and 16-31, as B operands
+
+  // Product phase of tile t: S^T(t) = K Q^T and dP^T(t) = V dO^T from stage CSTAGE
+  // (k-step major), then dQ^T += K^T(t-1) dS^T(t-1) with K^T read transposed
+  // from stage PSTAGE.  Between the dQ products the wave subtracts Delta from
+  // the landed dP.  The first phase (t = 0) adds dS = 0 times the resident tile
+  // 0; the last (t = nt) computes the products of the reloaded last tile and
+  // drops them.  Operands go through a register ring PF products deep, pinned by
+  // scheduling groups (as in the forward).
+  auto m_phase = [&](auto CSTAGE, auto PSTAGE) {
+    constexpr int cst = decltype(CSTAGE)::value, pst = decltype(PSTAGE)::value;
+    constexpr int NSD = 2 * NKS, NDQ = 2 * NDB, N = NSD + NDQ, PF = 3;
+    constexpr int SUB_PER = (16 + NDQ - 3) / (NDQ - 2);  // Delta subtractions per dQ product (after the first two)
+    static_assert(PF <= NSD, "the ring starts inside the score products");
+    auto rd = [&](int i) {
+      if (i < NSD) {  // K (even i) or V (odd i) operand of k-step i / 2
+        const int o = kbase + (((i >> 1) ^ kx) << 4) + ((i & 1) ? KT : 0);
+        return *reinterpret_cast<const u32x4*>(&KV[cst][o]);
+      }
+      const int kk = (i - NSD) / NDB, db = (i - NSD) % NDB;  // K^T operand of dQ product i - NSD
+      const u32x2 lo = ds_read_tr16(&KV[pst][tofs[0][db] + 16 * kk * D]);
+      const u32x2 hi = ds_read_tr16(&KV[pst][tofs[1][db] + 16 * kk * D]);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 fr[N];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) fr[i] = rd(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + PF < N) fr[i + PF] = rd(i + PF);
+      if (i < NSD) {
+        const int ks = i >> 1;
+        if (i & 1)
+          dpv = mfma32(as_bf16x8(fr[i]), of[ks], ks == 0 ? f32x16{} : dpv);
+        else
+          sc = mfma32(as_bf16x8(fr[i]), qf[ks], ks == 0 ? f32x16{} : sc);
+      } else {
+        const int j = i - NSD;
+        dqa[j % NDB] = mfma32(as_bf16x8(fr[i]), sb[j / NDB], dqa[j % NDB]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dpv[r] -= dl;
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // operands of the first PF products
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // product i
+      if (i + PF < NSD) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the read of score product i + PF
+      } else if (i + PF < N) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two reads of dQ product i + PF - NSD
+      }
+      if (i >= NSD + 2) __builtin_amdgcn_sched_group_barrier(0x002, SUB_PER, 0);  // Delta subtractions
+    }
+    asm volatile("" : "+v"(sc), "+v"(dpv));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(dqa[db]));
+  };
+
+  // Arithmetic phase of tile t: mask, P = exp2(S c - LSE2), dS = P (dP - Delta)
+  // (lse2 = +inf for a row without any allowed key, so its P is exactly 0),
+  // packed to bf16.
+  auto v_phase = [&](int t) {
+    if (classify(t) == kPartial) {
+      const int j0 = tile_of(t) * BK;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        s_cur[r] = in_window(kwin, j) ? s_cur[r] : NEG_INF;
+        sc[r] = in_window(kwin, j) ? sc[r] : NEG_INF;
       }
     }
-    // scores of tile t+1 interleaved with dS of tile t (lse2 = +inf for a row
-    // without any allowed key, so its probabilities are exactly 0)
     float dsv[16];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      score_k(std::integral_constant<int, nstage>{}, ks, s_nx, dp_nx);
+    for (int r = 0; r < 16; ++r) dsv[r] = fast_exp2(__builtin_fmaf(sc[r], c, -l2)) * dpv[r];
+    sb[0] = pack_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+    sb[1] = pack_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+    asm volatile("" : "+v"(sb[0]), "+v"(sb[1]));
+    asm volatile("" : "+v"(sc), "+v"(dpv));
 #pragma unroll
-      for (int u = 0; u < 16 / NKS; ++u) {
-        const int r = (16 / NKS) * ks + u;
-        const float pr = fast_exp2(__builtin_fmaf(s_cur[r], c, -l2));
-        dsv[r] = pr * (dp_cur[r] - dl);
-      }
-    }
-    const bf16x8 sb0 = pack_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-    const bf16x8 sb1 = pack_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-    // dQ^T += K^T dS^T; K^T read transposed from the row-major K tile, first 16 keys for every block, then
-    // the next 16 (the first products need only the first pack)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const u32x2 lo0 = ds_read_tr16(&KV[stage][tofs[0][db]]);
-      const u32x2 hi0 = ds_read_tr16(&KV[stage][tofs[1][db]]);
-      const u32x4 a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
-      dqa[db] = mfma32(as_bf16x8(a0), sb0, dqa[db]);
-    }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const u32x2 lo1 = ds_read_tr16(&KV[stage][tofs[0][db] + 16 * D]);
-      const u32x2 hi1 = ds_read_tr16(&KV[stage][tofs[1][db] + 16 * D]);
-      const u32x4 a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
-      dqa[db] = mfma32(as_bf16x8(a1), sb1, dqa[db]);
-    }
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(dqa[db]));
+  };
+
+  // Phase boundaries, as in the forward: phase 2m starts once tile m is
+  // resident for every wave, and then the load of tile m+2 goes into the stage
+  // tile m-2 held (its last reader, a dQ product, ran in phase 2m-1).
+  auto sync_even = [&](auto STAGE2, int m) {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_ring_sync<LOADS_PER_TILE>();
+    issue_tile(STAGE2, m + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto sync_odd = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   if (nt > 0) {
-    static_assert(NST == 4, "the loop below is unrolled for a ring of 4 stages");
+    static_assert(NST == 4, "the phase schedule below is written for a ring of 4 stages");
     using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
     issue_tile(S0{}, 0);
-    issue_tile(std::integral_constant<int, 1>{}, 1);
-    issue_tile(std::integral_constant<int, 2>{}, 2);
-    lds_ring_sync<(NST - 2) * LOADS_PER_TILE>();
-    int cls_a = classify(0), cls_b = kFull;
-    f32x16 s_a, dp_a, s_b, dp_b;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) score_k(S0{}, ks, s_a, dp_a);
-    for (int t = 0; t < nt; t += 4) {
-      step(S0{}, t, s_a, dp_a, cls_a, s_b, dp_b, cls_b);
-      if (t + 1 >= nt) break;
-      step(std::integral_constant<int, 1>{}, t + 1, s_b, dp_b, cls_b, s_a, dp_a, cls_a);
-      if (t + 2 >= nt) break;
-      step(std::integral_constant<int, 2>{}, t + 2, s_a, dp_a, cls_a, s_b, dp_b, cls_b);
-      if (t + 3 >= nt) break;
-      step(std::integral_constant<int, 3>{}, t + 3, s_b, dp_b, cls_b, s_a, dp_a, cls_a);
+    issue_tile(S1{}, 1);
+    sync_even(S2{}, 0);
+    // Ping-pong between the two waves of each SIMD (waves w and w + NW/2), as in
+    // the forward: the first half runs the product phase of tile t in phase 2t
+    // and its arithmetic in phase 2t+1, the second half one phase later; both
+    // pass the same 2*nt + 2 barriers.
+    if (w < Cfg::NW / 2) {
+      m_phase(S0{}, S0{});
+      for (int t0 = 0;; t0 += 4) {
+        sync_odd();
+        v_phase(t0);
+        sync_even(S3{}, t0 + 1);
+        m_phase(S1{}, S0{});
+        if (t0 + 1 == nt) break;
+        sync_odd();
+        v_phase(t0 + 1);
+        sync_even(S0{}, t0 + 2);
+        m_phase(S2{}, S1{});
+        if (t0 + 2 == nt) break;
+        sync_odd();
+        v_phase(t0 + 2);
+        sync_even(S1{}, t0 + 3);
+        m_phase(S3{}, S2{});
+        if (t0 + 3 == nt) break;
+        sync_odd();
+        v_phase(t0 + 3);
+        sync_even(S2{}, t0 + 4);
+        m_phase(S0{}, S3{});
+        if (t0 + 4 == nt) break;
+      }
+      sync_odd();
+    } else {
+      sync_odd();
+      m_phase(S0{}, S0{});
+      for (int t0 = 0;; t0 += 4) {
+        sync_even(S3{}, t0 + 1);
+        v_phase(t0);
+        sync_odd();
+        m_phase(S1{}, S0{});
+        if (t0 + 1 == nt) break;
+        sync_even(S0{}, t0 + 2);
+        v_phase(t0 + 1);
+        sync_odd();
+        m_phase(S2{}, S1{});
+        if (t0 + 2 == nt) break;
+        sync_even(S1{}, t0 + 3);
+        v_phase(t0 + 2);
+        sync_odd();
+        m_phase(S3{}, S2{});
+        if (t0 + 3 == nt) break;
+        sync_even(S2{}, t0 + 4);
+        v_phase(t0 + 3);
+        sync_odd();
+        m_phase(S0{}, S3{});
+        if (t0 + 4 == nt) break;
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // retire the trailing (unused) loads
   }
