@@ -6,7 +6,8 @@
 //  1. delta:  Delta_i = <dO_i, O_i>, one pass over O and dO (HBM-bound).
 //  2. dkdv:   one workgroup per 128-key block: 8 waves, two per SIMD, in pairs
 //             sharing 32 keys (one wave holds K and produces P and dV, the
-//             other holds V and produces dS and dK; P crosses over in LDS).
+//             other holds V and produces dS and dK; P crosses over in LDS);
+//             the pair alternates product and vector phases (ping-pong).
 //             32-row query tiles (Q, dO, LSE, Delta) stream through a
 //             direct-to-LDS ring.  Scores are computed with the key on the MFMA
 //             column (lane) axis, so P and dS come out of the MFMA already in
@@ -137,12 +138,13 @@ __device__ __forceinline__ void rope_back(f32x16 (&acc)[NDB], int pos, const dou
 // inverse power of two.
 //
 // 32-row query tiles (Q, dO, LSE, Delta) stream through a 6-stage LDS ring of
-// direct global->LDS loads (tiles t-1 .. t+1 in use, t+2 .. t+4 in flight).  In
-// step t, A computes the scores of tile t+1 while turning those of tile t into
-// P (software pipeline) and publishes P(t); B computes dP(t) while forming
-// dS(t-1) from P(t-1), published one step earlier, so the one workgroup barrier
-// per step orders both the ring and the exchange.  Each role runs its own copy
-// of the loop so that its accumulator stays in the same registers.
+// direct global->LDS loads, issued four tiles ahead.  The two waves of a SIMD
+// (A and B of one key group) run a ping-pong: in phase 2t A issues the products
+// of tile t (S(t), dV += dO(t-1)^T P(t-1)) while B forms dS(t-1); in phase 2t+1
+// A turns S(t) into P(t) and hands it to B while B issues its products (dP(t),
+// dK += Q(t-1)^T dS(t-1)).  Workgroup barriers separate the phases and order
+// both the ring and the hand-over.  Each role runs its own copy of the loop so
+// that its accumulator stays in the same registers.
 // The dK/dV pass works with P * 2^kPScaleLog2 (see the fp16 hand-over below).
 constexpr int kPScaleLog2 = 14;
 
@@ -316,41 +318,36 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     return kmax_w <= qmn ? (int)kFull : (int)kPartial;
   };
 
-  // one k-step of the score product with this wave's operand (S for A with Q,
-  // dP for B with dO) for the tile in stage STAGE; output register r of lane l
-  // holds query 8*(r/4) + 4*g + r%4 of key ln
-  auto score_k = [&](auto ROLE, int stage, int ks, f32x16& s) {
-    const int o = qbase + ((ks ^ qx) << 4) + decltype(ROLE)::value * OT;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(&QO[stage][o]);
-    s = mfma32(as_bf16x8(a), kvf[ks], ks == 0 ? f32x16{} : s);
-  };
-  auto scores = [&](auto ROLE, int stage, f32x16& s) {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) score_k(ROLE, stage, ks, s);
-  };
+  using RoleA = std::integral_constant<int, 0>;
+  using RoleB = std::integral_constant<int, 1>;
+  const float c = p.c;
+  constexpr float NEG_INF = -__builtin_inff();
 
-  // bf16 packs of a lane's 16 values: pk[kk] holds values 8*kk .. 8*kk+7
-  auto pack16 = [&](const float* v, bf16x8* pk) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int o = 8 * kk;
-      pk[kk] = pack_bf16x8(v[o], v[o + 1], v[o + 2], v[o + 3], v[o + 4], v[o + 5], v[o + 6], v[o + 7]);
-    }
-  };
-  // acc += (tile^T operand) x (the packs), two 16-query k-steps; the transposed
-  // operand is dO (A: dV) or Q (B: dK) of the tile in stage STAGE
-  //
-  // The transposed operands go through a register ring two products deep (the
-  // reads of product i+2 are issued before product i), pinned by scheduling
-  // groups: left to itself the compiler read each operand right before its
-  // product and waited for it, so one wave spent an LDS latency per product.
-  auto accumulate = [&](auto ROLE, int stage, const bf16x8* pk) {
-    constexpr int base = decltype(ROLE)::value == 0 ? OT : 0;
-    constexpr int N = 2 * NDB, PF = 2;  // products (k-step major), read distance
+  // Ping-pong between the two waves of each SIMD (A = wave kw, B = wave 4 + kw,
+  // same keys).  Phase 2t: A runs its product phase of query tile t (S(t), then
+  // dV^T += dO(t-1)^T P(t-1)) while B forms dS(t-1) = P(t-1) (dP(t-1) - Delta);
+  // phase 2t+1: A turns S(t) into P(t) and hands it to B through LDS while B runs
+  // its product phase (dP(t), then dK^T += Q(t-1)^T dS(t-1)).  So in every phase
+  // one wave of each SIMD feeds the matrix core and the other runs vector work;
+  // workgroup barriers separate the phases.
+  f32x16 sx;                             // A: S of the current tile; B: dP
+  bf16x8 pk[2] = {bf16x8{}, bf16x8{}};   // A: P of the previous tile; B: dS of the previous tile (bf16)
+
+  // product phase: the score-like product of tile (stage cst) with this wave's
+  // K or V rows, then acc += (tile^T operand of stage pst) x pk, the transposed
+  // operand being dO (A: dV) or Q (B: dK).  Operands through a register ring PF
+  // products deep, pinned by scheduling groups (left to itself the compiler read
+  // each operand right before its product and waited for it).
+  auto m_phase = [&](auto ROLE, auto CST, auto PST) {
+    constexpr int R = decltype(ROLE)::value, cst = decltype(CST)::value, pst = decltype(PST)::value;
+    constexpr int NSC = NKS, NAC = 2 * NDB, N = NSC + NAC, PF = 3;
+    static_assert(PF <= NSC, "the ring starts inside the score products");
     auto rd = [&](int i) {
-      const int kk = i / NDB, db = i % NDB;
-      const u32x2 lo = ds_read_tr16(&QO[stage][base + tofs[0][db] + 16 * kk * D]);
-      const u32x2 hi = ds_read_tr16(&QO[stage][base + tofs[1][db] + 16 * kk * D]);
+      if (i < NSC) return *reinterpret_cast<const u32x4*>(&QO[cst][qbase + ((i ^ qx) << 4) + R * OT]);
+      const int kk = (i - NSC) / NDB, db = (i - NSC) % NDB;
+      constexpr int base = R == 0 ? OT : 0;
+      const u32x2 lo = ds_read_tr16(&QO[pst][base + tofs[0][db] + 16 * kk * D]);
+      const u32x2 hi = ds_read_tr16(&QO[pst][base + tofs[1][db] + 16 * kk * D]);
       return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
     u32x4 fr[N];
@@ -359,45 +356,55 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       if (i + PF < N) fr[i + PF] = rd(i + PF);
-      acc[i % NDB] = mfma32(as_bf16x8(fr[i]), pk[i / NDB], acc[i % NDB]);
+      if (i < NSC) {
+        sx = mfma32(as_bf16x8(fr[i]), kvf[i], i == 0 ? f32x16{} : sx);
+      } else {
+        const int j = i - NSC;
+        acc[j % NDB] = mfma32(as_bf16x8(fr[i]), pk[j / NDB], acc[j % NDB]);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);  // the first PF products' reads
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // operands of the first PF products
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // product i
-      if (i + PF < N) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of product i + PF
+      if (i + PF < NSC) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the read of score product i + PF
+      } else if (i + PF < N) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two reads of product i + PF
+      }
     }
+    asm volatile("" : "+v"(sx));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(acc[db]));
   };
 
-  const float c = p.c;
-  constexpr float NEG_INF = -__builtin_inff();
-  using RA = std::integral_constant<int, 0>;
-  using RB = std::integral_constant<int, 1>;
+  // bf16 packs of a lane's 16 values: pk[kk] holds values 8*kk .. 8*kk+7
+  auto pack16 = [&](const float* v) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int o = 8 * kk;
+      pk[kk] = pack_bf16x8(v[o], v[o + 1], v[o + 2], v[o + 3], v[o + 4], v[o + 5], v[o + 6], v[o + 7]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) asm volatile("" : "+v"(pk[kk]));
+  };
 
-  // ---- role A, step t: P(t) from the scores of tile t (in s_cur), interleaved
-  // with the scores of tile t+1; publish P(t); dV^T += dO(t)^T P(t)
-  auto step_a = [&](int stage, int t, f32x16& s_cur, int& cls_cur, f32x16& s_nx, int& cls_nx) {
-    const int nstage = stage + 1 == NST ? 0 : stage + 1;
-    const int i0 = tile_of(t) * BQ;
-    cls_nx = t + 1 < nt ? classify(t + 1) : (int)kFull;
-    if (cls_cur == kPartial) {
+  // A's vector phase for tile t (stage st): mask, P = exp2(S c - LSE2) (the LSE
+  // of the tile's rows is already in base-2 units, see to_log2), published to
+  // B as fp16 pairs, kept as bf16 packs for dV.
+  auto a_v = [&](auto ST, int t) {
+    constexpr int st = decltype(ST)::value;
+    if (classify(t) == kPartial) {
+      const int i0 = tile_of(t) * BQ;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        s_cur[r] = in_window(qwin, i) ? s_cur[r] : NEG_INF;
+        sx[r] = in_window(qwin, i) ? sx[r] : NEG_INF;
       }
     }
-    // the LSE of the tile's rows is already in base-2 units (see to_log2 below)
     float pv[16];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      score_k(RA{}, nstage, ks, s_nx);
-#pragma unroll
-      for (int u = 0; u < 16 / NKS; ++u) {
-        const int r = (16 / NKS) * ks + u;
-        pv[r] = fast_exp2(__builtin_fmaf(s_cur[r], c, -Ss[stage][8 * (r >> 2) + 4 * g + (r & 3)]));
-      }
-    }
+    for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(sx[r], c, -Ss[st][8 * (r >> 2) + 4 * g + (r & 3)]));
     uint32_t* pdst = &Ps[t & 1][kw][0][lane][0];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -406,125 +413,117 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
       for (int e = 0; e < 4; ++e) hv[e] = pack_f16x2(pv[8 * j + 2 * e], pv[8 * j + 2 * e + 1]);
       *reinterpret_cast<u32x4*>(pdst + j * 256) = hv;
     }
-    bf16x8 pk[2];
-    pack16(pv, pk);
-    accumulate(RA{}, stage, pk);
+    pack16(pv);
   };
 
-  // ---- role B, step t: dP(t) (into dp_nx) interleaved with dS(t-1) from P(t-1)
-  // and dP(t-1) (in dp_cur); dK^T += Q(t-1)^T dS(t-1).  PSTAGE = stage of t-1.
-  auto step_b = [&](int stage, int pstage, auto DO_DP, int t, f32x16& dp_cur, f32x16& dp_nx) {
-    constexpr bool do_dp = decltype(DO_DP)::value;  // false: last step, no tile t
-    constexpr int PF = 2;                           // read distance of the dO operands
-    const bool prev = t > 0;
+  // B's vector phase for tile t (stage st): dS = P (dP - Delta) from A's P(t).
+  auto b_v = [&](auto ST, int t) {
+    constexpr int st = decltype(ST)::value;
+    const u32x4* psrc8 = reinterpret_cast<const u32x4*>(&Ps[t & 1][kw][0][lane][0]);
+    const f32x4* dsrc4 = reinterpret_cast<const f32x4*>(&Ss[st][BQ + 4 * g]);
+    const u32x4 ph[2] = {psrc8[0], psrc8[64]};
     float dsv[16];
-    // P(t-1) (fp16 pairs, eight values per 16 bytes) and Delta of the 16 queries this lane holds
-    const u32x4* psrc8 = reinterpret_cast<const u32x4*>(&Ps[(t + 1) & 1][kw][0][lane][0]);
-    const f32x4* dsrc4 = reinterpret_cast<const f32x4*>(&Ss[pstage][BQ + 4 * g]);
-    auto rd = [&](int ks) {
-      return *reinterpret_cast<const u32x4*>(&QO[stage][qbase + ((ks ^ qx) << 4) + OT]);
-    };
-    u32x4 fr[NKS];
-    if constexpr (do_dp) {
 #pragma unroll
-      for (int i = 0; i < PF; ++i) fr[i] = rd(i);
-    }
-    u32x4 ph[2];
-    f32x4 dm[4];
-    ph[0] = psrc8[0];
-    dm[0] = dsrc4[0];
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 dm = dsrc4[2 * m];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if constexpr (do_dp) {
-        if (ks + PF < NKS) fr[ks + PF] = rd(ks + PF);
-        dp_nx = mfma32(as_bf16x8(fr[ks]), kvf[ks], ks == 0 ? f32x16{} : dp_nx);
-      }
-      constexpr int GS = NKS / 4;  // k-steps per group of four values (two at D = 128, one at D = 64)
-      if (ks % GS == 0) {
-        const int m = ks / GS;
-        if (m + 1 < 4) dm[m + 1] = dsrc4[2 * (m + 1)];
-        if (m == 0) ph[1] = psrc8[64];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * m + e;
-          const float pr = unpack_f16(ph[r >> 3][(r & 7) >> 1], r & 1);
-          const float ds = pr * (dp_cur[r] - dm[m][e]);
-          dsv[r] = prev ? ds : 0.f;  // step 0 has no tile t-1: add zeros (keeps the accumulation unconditional)
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * m + e;
+        const float pr = unpack_f16(ph[r >> 3][(r & 7) >> 1], r & 1);
+        dsv[r] = pr * (sx[r] - dm[e]);
       }
     }
-    bf16x8 pk[2];
-    pack16(dsv, pk);
-    // at step 0 the zeros multiply tile 0's Q (resident, finite) rather than a stage never loaded
-    accumulate(RB{}, prev ? pstage : stage, pk);
+    pack16(dsv);
+    asm volatile("" : "+v"(sx));
   };
 
-  // Wave 0, which loads the per-row statistics, rewrites the LSE of a resident
-  // tile in base-2 units less kPScaleLog2, so that exp2 gives 2^kPScaleLog2 P
-  // (-inf, a row without any allowed key, becomes +inf so that its recomputed
-  // probabilities are exactly 0); the next barrier publishes the converted
-  // values.
-  auto to_log2 = [&](int stage) {
-    if (w == 0 && g == 0) {
+  // Wave 4 (a V-side wave, in a vector phase when the tile arrives) rewrites the
+  // LSE of a resident tile in base-2 units less kPScaleLog2, so that exp2 gives
+  // 2^kPScaleLog2 P (-inf, a row without any allowed key, becomes +inf so that
+  // its recomputed probabilities are exactly 0); the next barrier publishes the
+  // converted values before A's vector phase reads them.
+  auto to_log2 = [&](auto ST) {
+    constexpr int stage = decltype(ST)::value;
+    if (w == 4 && g == 0) {
       const float l = Ss[stage][ln];
       Ss[stage][ln] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e - kPScaleLog2;
     }
   };
 
-  if (nt > 0) {
-    constexpr int AHEAD = NST - 4;  // tiles still in flight when tile t+1 must be resident
-    for (int i = 0; i < NST - 2; ++i) issue_tile(i, i);
-    wait_ring(std::integral_constant<int, AHEAD>{});  // tiles 0 and 1 resident
-    to_log2(0);
+  // Phase 2m starts once tile m is resident for every wave; then the loads of
+  // tile m+4 go into the stage tile m-2 held (its last reader, a dK product, ran
+  // in phase 2m-1).  Odd phases start with a barrier alone.
+  constexpr int AHEAD = 3;  // tiles in flight beyond the one needed
+  static_assert(NST == 6, "loads run four tiles ahead in a ring of six stages");
+  auto sync_even = [&](auto STAGE4, int m) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_ring(std::integral_constant<int, AHEAD>{});
+    issue_tile(decltype(STAGE4)::value, m + 4);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto sync_odd = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // Step t reads tiles t-1, t, t+1 and loads tile t+NST-2 into the stage of
-    // tile t-2.  Unrolled by two so that the two score buffers alternate.  Each
-    // role runs its own copy of the loop (the role is uniform per wave), so that
-    // its accumulators keep their registers from one iteration to the next.
-    auto run = [&](auto ROLE) {
-      constexpr int R = decltype(ROLE)::value;
-      f32x16 sa, sb;  // role A: scores; role B: dP
-      int ca = kFull, cb = kFull;
-      if constexpr (R == 0) {
-        ca = classify(0);
-        scores(RA{}, 0, sa);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  // step t of each role with every stage index a constant (t = 6 i + U): tile
+  // t in stage U, tile t+1 in stage U+1, loads of tile t+5 into stage U+5
+  auto a_step = [&](auto U, int t) {
+    constexpr int u = decltype(U)::value;
+    using ST = std::integral_constant<int, u % NST>;
+    using SN = std::integral_constant<int, (u + 1) % NST>;
+    using SL = std::integral_constant<int, (u + 5) % NST>;
+    sync_odd();
+    a_v(ST{}, t);
+    sync_even(SL{}, t + 1);
+    m_phase(RoleA{}, SN{}, ST{});
+    return t + 1 < nt;
+  };
+  auto b_step = [&](auto U, int t) {
+    constexpr int u = decltype(U)::value;
+    using ST = std::integral_constant<int, u % NST>;
+    using SN = std::integral_constant<int, (u + 1) % NST>;
+    using SL = std::integral_constant<int, (u + 5) % NST>;
+    sync_even(SL{}, t + 1);
+    b_v(ST{}, t);
+    to_log2(SN{});
+    sync_odd();
+    m_phase(RoleB{}, SN{}, ST{});
+    return t + 1 < nt;
+  };
+
+  if (nt > 0) {
+    for (int i = 0; i < 4; ++i) issue_tile(i, i);
+    sync_even(std::integral_constant<int, 4>{}, 0);
+    // Both roles pass the same 2*nt + 2 barriers.  The first product phase of
+    // each role adds zeros times the resident tile 0, the last one computes the
+    // score-like product of the reloaded last tile and drops it, so every
+    // product phase is the same straight run of products.
+    if (role == 0) {
+      m_phase(RoleA{}, S0{}, S0{});
+      for (int t = 0;; t += 6) {
+        if (!a_step(std::integral_constant<int, 0>{}, t)) break;
+        if (!a_step(std::integral_constant<int, 1>{}, t + 1)) break;
+        if (!a_step(std::integral_constant<int, 2>{}, t + 2)) break;
+        if (!a_step(std::integral_constant<int, 3>{}, t + 3)) break;
+        if (!a_step(std::integral_constant<int, 4>{}, t + 4)) break;
+        if (!a_step(std::integral_constant<int, 5>{}, t + 5)) break;
       }
-      int st = 0;  // stage of tile t
-      auto body = [&](int t, f32x16& x_cur, int& c_cur, f32x16& x_nx, int& c_nx) {
-        if (t > 0) wait_ring(std::integral_constant<int, AHEAD>{});  // tile t+1 resident; all past step t-1
-        const int sp = st == 0 ? NST - 1 : st - 1;
-        const int sf = st >= 2 ? st - 2 : st + NST - 2;
-        issue_tile(sf, t + NST - 2);
-        if constexpr (R == 0) {
-          to_log2(st + 1 == NST ? 0 : st + 1);  // tile t+1, read from step t+1 on
-          step_a(st, t, x_cur, c_cur, x_nx, c_nx);
-        } else {
-          step_b(st, sp, std::true_type{}, t, x_cur, x_nx);
-        }
-        st = st + 1 == NST ? 0 : st + 1;
-      };
-      for (int t = 0; t < nt; t += 2) {
-        body(t, sa, ca, sb, cb);
-        if (t + 1 >= nt) break;
-        body(t + 1, sb, cb, sa, ca);
+      sync_odd();
+    } else {
+      to_log2(S0{});
+      sync_odd();
+      m_phase(RoleB{}, S0{}, S0{});
+      for (int t = 0;; t += 6) {
+        if (!b_step(std::integral_constant<int, 0>{}, t)) break;
+        if (!b_step(std::integral_constant<int, 1>{}, t + 1)) break;
+        if (!b_step(std::integral_constant<int, 2>{}, t + 2)) break;
+        if (!b_step(std::integral_constant<int, 3>{}, t + 3)) break;
+        if (!b_step(std::integral_constant<int, 4>{}, t + 4)) break;
+        if (!b_step(std::integral_constant<int, 5>{}, t + 5)) break;
       }
-      // role B's last step: dS and dK of tile nt-1 (P(nt-1) published in step nt-1)
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if constexpr (R == 1) {
-        f32x16 last = (nt % 2 == 1) ? sb : sa;  // dP(nt-1): into sb for even nt-1, sa for odd
-        f32x16 dummy;
-        const int sp = st == 0 ? NST - 1 : st - 1;  // st is now the stage of tile nt
-        step_b(st, sp, std::false_type{}, nt, last, dummy);
-      }
-    };
-    // both roles at the default issue priority: with the operand rings above, raising the V-side waves'
-    // priority (which helped when they waited on every operand) costs 2 %
-    if (role == 0)
-      run(RA{});
-    else
-      run(RB{});
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // retire the trailing (unused) loads
   }
 
