@@ -391,7 +391,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 
   // A's vector phase for tile t (stage st): mask, P = exp2(S c - LSE2) (the LSE
   // of the tile's rows is already in base-2 units, see to_log2), published to
-  // B as fp16 pairs, kept as bf16 packs for dV.
+  // B as fp16 pairs, kept as bf16 packs for dV.  A barrier does not wait for
+  // memory, so A waits for its LDS writes before the barrier that publishes them.
   auto a_v = [&](auto ST, int t) {
     constexpr int st = decltype(ST)::value;
     if (classify(t) == kPartial) {
@@ -414,6 +415,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
       *reinterpret_cast<u32x4*>(pdst + j * 256) = hv;
     }
     pack16(pv);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
   // B's vector phase for tile t (stage st): dS = P (dP - Delta) from A's P(t).
@@ -441,13 +443,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   // LSE of a resident tile in base-2 units less kPScaleLog2, so that exp2 gives
   // 2^kPScaleLog2 P (-inf, a row without any allowed key, becomes +inf so that
   // its recomputed probabilities are exactly 0); the next barrier publishes the
-  // converted values before A's vector phase reads them.
+  // converted values before A's vector phase reads them (wave 4 waits for its
+  // write first: a barrier does not wait for memory).
   auto to_log2 = [&](auto ST) {
     constexpr int stage = decltype(ST)::value;
     if (w == 4 && g == 0) {
       const float l = Ss[stage][ln];
       Ss[stage][ln] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e - kPScaleLog2;
     }
+    if (w == 4) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
   // Phase 2m starts once tile m is resident for every wave; then the loads of
@@ -463,7 +467,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   };
   auto sync_odd = [&]() {
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
   using S0 = std::integral_constant<int, 0>;
@@ -795,7 +801,9 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
   };
   auto sync_odd = [&]() {
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
 

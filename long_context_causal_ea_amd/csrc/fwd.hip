@@ -391,7 +391,9 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   };
   auto sync_odd = [&]() {
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
 
