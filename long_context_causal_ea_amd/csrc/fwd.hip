@@ -168,17 +168,18 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   const int nt = nA + nB;
   auto tile_of = [&](int t) { return t < nA ? t : tB0 + (t - nA); };
 
-  // ---- running statistics (raw-score units for the max)
+  // ---- running statistics, in base-2 units: each score s becomes
+  // z = s*c - moff, moff being the row's running offset (the running maximum of
+  // s*c, up to rounding), and P = exp2(z).  The offset is raised only when a
+  // tile's z exceeds 8: probabilities then stay below 2^8, exactly representable
+  // in the accumulation, and the rescale of O is rare.  -inf: no score yet.
   constexpr float NEG_INF = -__builtin_inff();
-  // The running maximum is raised only when a tile's maximum exceeds it by more
-  // than 8 (in log2 units): probabilities then stay below 2^8, exactly
-  // representable in the accumulation, and the rescale of O is rare.
-  const float raise_thr = 8.f / p.c;
+  constexpr float kLn2 = 0.693147180559945309f;
   // The row sum is kept as four partial sums (summed at the end) and the row
-  // maximum of a tile is formed by four independent chains: a softmax phase
-  // runs alone on its SIMD's vector ALU, so its dependency chains are not
-  // hidden behind another wave's work.
-  float m_run = NEG_INF, l_run[4] = {0.f, 0.f, 0.f, 0.f};
+  // maximum of a tile is formed by four independent chains: each phase runs
+  // alone on its SIMD's vector ALU, so its dependency chains are not hidden
+  // behind another wave's work.
+  float moff = NEG_INF, l_run[4] = {0.f, 0.f, 0.f, 0.f};
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   f32x16 st[NMB];         // S^T of the tile between its product phase and its softmax phase
   bf16x8 pb[2 * NMB];     // P^T as B operands, one per 16-key k-step, until the next product phase
   float ep[16 * NMB];     // the same probabilities in fp32, added to the row sums in the next product phase
-  float mx_t = NEG_INF;   // row maximum of the tile's scores, formed in its product phase
+  float mx_t = NEG_INF;   // row maximum of the tile's z, formed in its product phase
 #pragma unroll
   for (int kk = 0; kk < 2 * NMB; ++kk) pb[kk] = bf16x8{};
 #pragma unroll
@@ -282,13 +283,15 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   // products deep, pinned by scheduling groups (left to itself the compiler read
   // each K operand right before its product and waited for it).  Between the
   // products the wave adds the previous tile's probabilities to its row sums and,
-  // once the scores have landed, forms their row maximum: vector work that
-  // would otherwise lengthen the softmax phase, which runs alone on its vector ALU.
+  // once the scores have landed, turns them into z = s*c - moff and forms their
+  // row maximum: vector work that would otherwise lengthen the softmax phase,
+  // which runs alone on its vector ALU.
   auto m_phase = [&](auto KSTAGE, auto VSTAGE) {
     constexpr int kstage = decltype(KSTAGE)::value, vstage = decltype(VSTAGE)::value;
     constexpr int NS = NKS * NMB, NPV = 2 * NMB * NDB, N = NS + NPV, PF = 3;
+    __builtin_amdgcn_s_setprio(2);  // the products win the issue port from the other wave's vector work
     constexpr int ADD_PER = (16 * NMB + NS - 1) / NS;     // row-sum adds per score product
-    constexpr int MAX_PER = (24 + NPV - 3) / (NPV - 2);  // row-maximum work per O product (after the first two)
+    constexpr int MAX_PER = (56 + NPV - 3) / (NPV - 2);  // z and row-maximum work per O product (after the first two)
     static_assert(PF <= NS, "the ring starts inside the score products");
     auto rd = [&](int i) {
       if (i < NS) {  // K operand of score product i (k-step major)
@@ -317,6 +320,11 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
     }
 #pragma unroll
     for (int r = 0; r < 16 * NMB; ++r) l_run[r & 3] += ep[r];
+    const float msub = moff == NEG_INF ? 0.f : moff;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[mb][r] = __builtin_fmaf(st[mb][r], p.c, -msub);
     mx_t = row_max();
     __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // operands of the first PF products
 #pragma unroll
@@ -330,15 +338,16 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
       if (i < NS) {
         __builtin_amdgcn_sched_group_barrier(0x002, ADD_PER, 0);  // row-sum adds
       } else if (i >= NS + 2) {
-        __builtin_amdgcn_sched_group_barrier(0x002, MAX_PER, 0);  // row maximum of the new scores
+        __builtin_amdgcn_sched_group_barrier(0x002, MAX_PER, 0);  // z and row maximum of the new scores
       }
     }
     pin_phase_outputs(st, oacc);
     asm volatile("" : "+v"(mx_t), "+v"(l_run[0]), "+v"(l_run[1]), "+v"(l_run[2]), "+v"(l_run[3]));
+    __builtin_amdgcn_s_setprio(0);
   };
 
-  // Softmax phase of tile t: mask (the maximum is then formed again), rescale,
-  // exponentials, P^T packed to bf16.
+  // Softmax phase of tile t: mask (the maximum is then formed again), raise of
+  // the offset (rare), exponentials, P^T packed to bf16.
   auto v_phase = [&](int t) {
     const int j0 = tile_of(t) * BK;
     float mx = mx_t;
@@ -352,21 +361,25 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
         }
       mx = row_max();
     }
-    if (__any(mx > m_run + raise_thr)) {
-      const float mnew = fmaxf(m_run, mx);
-      const float alpha = (m_run == NEG_INF) ? 0.f : fast_exp2((m_run - mnew) * p.c);
+    // raise when some z exceeds 8, or on a row's first finite scores (its z are
+    // then s*c, unshifted); every row of the wave takes the larger of its offset
+    // and its maximum
+    if (__any(mx > (moff == NEG_INF ? NEG_INF : 8.f))) {
+      const float shift = moff == NEG_INF ? (mx == NEG_INF ? 0.f : mx) : fmaxf(mx, 0.f);
+      const float alpha = moff == NEG_INF ? 0.f : fast_exp2(-shift);
 #pragma unroll
       for (int i = 0; i < 4; ++i) l_run[i] *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      m_run = mnew;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) st[mb] -= shift;
+      moff = moff == NEG_INF ? (mx == NEG_INF ? NEG_INF : mx) : moff + shift;
     }
-    const float msub = (m_run == NEG_INF) ? 0.f : m_run * p.c;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       float* e = ep + 16 * mb;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(__builtin_fmaf(st[mb][r], p.c, -msub));
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(st[mb][r]);
       pb[2 * mb] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       pb[2 * mb + 1] = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
     }
@@ -374,7 +387,7 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
     for (int kk = 0; kk < 2 * NMB; ++kk) asm volatile("" : "+v"(pb[kk]));
 #pragma unroll
     for (int r = 0; r < 16 * NMB; ++r) asm volatile("" : "+v"(ep[r]));
-    asm volatile("" : "+v"(l_run[0]), "+v"(l_run[1]), "+v"(l_run[2]), "+v"(l_run[3]), "+v"(m_run));
+    asm volatile("" : "+v"(l_run[0]), "+v"(l_run[1]), "+v"(l_run[2]), "+v"(l_run[3]), "+v"(moff));
     pin_phase_outputs(st, oacc);
   };
 
@@ -479,7 +492,7 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
     // a side at -inf contributing nothing (the same arithmetic as merge_kernel)
     float* op = static_cast<float*>(p.o) + b * p.q_bstride + (long)h * D_ + (long)qrow * p.rs;
     const float l1 = p.lse[lse_at];
-    const float l2 = has ? (m_run * p.scale + logf(lt)) : NEG_INF;
+    const float l2 = has ? (moff * kLn2 + logf(lt)) : NEG_INF;
     const float mx = fmaxf(l1, l2), mn = fminf(l1, l2);
     const float L = (mx == NEG_INF) ? NEG_INF : mx + log1pf(expf(mn - mx));
     const float w1 = (L == NEG_INF) ? 0.f : expf(l1 - L);
@@ -522,7 +535,7 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
       }
   }
   if (g == 0) {
-    const float lse = has ? (m_run * p.scale + logf(lt)) : NEG_INF;
+    const float lse = has ? (moff * kLn2 + logf(lt)) : NEG_INF;
     p.lse[lse_at] = lse;
   }
 }
