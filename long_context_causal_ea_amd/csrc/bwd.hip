@@ -19,8 +19,8 @@
 //             dP^T with the query on the lane axis and accumulates
 //             dQ^T += K^T dS^T in registers (K^T by transpose read of the
 //             row-major K tile).  Like the forward it runs a ping-pong between
-//             the two waves of each SIMD: product phases and arithmetic phases
-//             one phase apart, between workgroup barriers.
+//             the two waves of each SIMD: product and arithmetic phases in
+//             opposite orders between the workgroup barriers.
 // All LDS tiles are row-major with the XOR chunk swizzle of ea_device.h.
 // The dq pass recomputes the two score products instead of exchanging dS
 // through atomics (fp32 atomic adds into L2 were measured at about 1.4 TB/s on
@@ -139,12 +139,12 @@ __device__ __forceinline__ void rope_back(f32x16 (&acc)[NDB], int pos, const dou
 //
 // 32-row query tiles (Q, dO, LSE, Delta) stream through a 6-stage LDS ring of
 // direct global->LDS loads, issued four tiles ahead.  The two waves of a SIMD
-// (A and B of one key group) run a ping-pong: in phase 2t A issues the products
-// of tile t (S(t), dV += dO(t-1)^T P(t-1)) while B forms dS(t-1); in phase 2t+1
-// A turns S(t) into P(t) and hands it to B while B issues its products (dP(t),
-// dK += Q(t-1)^T dS(t-1)).  Workgroup barriers separate the phases and order
-// both the ring and the hand-over.  Each role runs its own copy of the loop so
-// that its accumulator stays in the same registers.
+// (A and B of one key group) run a ping-pong: in step t A issues the products
+// of tile t (S(t), dV += dO(t-1)^T P(t-1)), then turns S(t) into P(t) and hands
+// it to B; B forms dS(t-1), then issues its products (dP(t),
+// dK += Q(t-1)^T dS(t-1)).  One workgroup barrier per step orders both the ring
+// and the hand-over.  Each role runs its own copy of the loop so that its
+// accumulator stays in the same registers.
 // The dK/dV pass works with P * 2^kPScaleLog2 (see the fp16 hand-over below).
 constexpr int kPScaleLog2 = 14;
 
@@ -324,12 +324,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   constexpr float NEG_INF = -__builtin_inff();
 
   // Ping-pong between the two waves of each SIMD (A = wave kw, B = wave 4 + kw,
-  // same keys).  Phase 2t: A runs its product phase of query tile t (S(t), then
-  // dV^T += dO(t-1)^T P(t-1)) while B forms dS(t-1) = P(t-1) (dP(t-1) - Delta);
-  // phase 2t+1: A turns S(t) into P(t) and hands it to B through LDS while B runs
-  // its product phase (dP(t), then dK^T += Q(t-1)^T dS(t-1)).  So in every phase
-  // one wave of each SIMD feeds the matrix core and the other runs vector work;
-  // workgroup barriers separate the phases.
+  // same keys).  In step t (between two workgroup barriers) A runs its product
+  // phase of query tile t (S(t), then dV^T += dO(t-1)^T P(t-1)), then turns S(t)
+  // into P(t) and hands it to B through LDS; B forms dS(t-1) = P(t-1) (dP(t-1) -
+  // Delta), then runs its product phase (dP(t), then dK^T += Q(t-1)^T dS(t-1)).
+  // So one wave of each SIMD tends to feed the matrix core while the other runs
+  // vector work.  (A second barrier per step that forced the phases apart cost
+  // more in waiting than it gained.)
   f32x16 sx;                             // A: S of the current tile; B: dP
   bf16x8 pk[2] = {bf16x8{}, bf16x8{}};   // A: P of the previous tile; B: dS of the previous tile (bf16)
 
@@ -439,12 +440,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     asm volatile("" : "+v"(sx));
   };
 
-  // Wave 4 (a V-side wave, in a vector phase when the tile arrives) rewrites the
-  // LSE of a resident tile in base-2 units less kPScaleLog2, so that exp2 gives
+  // Wave 4 (a V-side wave) rewrites the LSE of tile t+1 in base-2 units less
+  // kPScaleLog2 during step t, after its vector phase, so that exp2 gives
   // 2^kPScaleLog2 P (-inf, a row without any allowed key, becomes +inf so that
   // its recomputed probabilities are exactly 0); the next barrier publishes the
-  // converted values before A's vector phase reads them (wave 4 waits for its
-  // write first: a barrier does not wait for memory).
+  // converted values before A's vector phase of step t+1 reads them (wave 4
+  // waits for its write first: a barrier does not wait for memory).
   auto to_log2 = [&](auto ST) {
     constexpr int stage = decltype(ST)::value;
     if (w == 4 && g == 0) {
@@ -454,10 +455,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     if (w == 4) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
-  // Phase 2m starts once tile m is resident for every wave; then the loads of
-  // tile m+4 go into the stage tile m-2 held (its last reader, a dK product, ran
-  // in phase 2m-1).  Odd phases start with a barrier alone.
-  constexpr int AHEAD = 3;  // tiles in flight beyond the one needed
+  // Step m starts once tiles m and m+1 are resident for every wave (tile m+1
+  // for the LSE conversion); then the loads of tile m+4 go into the stage tile
+  // m-2 held (its last readers, the dV and dK products of tile m-2, ran in step
+  // m-1).
+  constexpr int AHEAD = 2;  // tiles in flight beyond the two needed
   static_assert(NST == 6, "loads run four tiles ahead in a ring of six stages");
   auto sync_even = [&](auto STAGE4, int m) {
     __builtin_amdgcn_sched_barrier(0);
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     issue_tile(decltype(STAGE4)::value, m + 4);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto sync_odd = [&]() {
+  auto sync_plain = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -480,7 +482,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     using ST = std::integral_constant<int, u % NST>;
     using SN = std::integral_constant<int, (u + 1) % NST>;
     using SL = std::integral_constant<int, (u + 5) % NST>;
-    sync_odd();
+    __builtin_amdgcn_sched_barrier(0);
     a_v(ST{}, t);
     sync_even(SL{}, t + 1);
     m_phase(RoleA{}, SN{}, ST{});
@@ -491,10 +493,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     using ST = std::integral_constant<int, u % NST>;
     using SN = std::integral_constant<int, (u + 1) % NST>;
     using SL = std::integral_constant<int, (u + 5) % NST>;
+    using SNN = std::integral_constant<int, (u + 2) % NST>;
     sync_even(SL{}, t + 1);
     b_v(ST{}, t);
-    to_log2(SN{});
-    sync_odd();
+    to_log2(SNN{});
+    __builtin_amdgcn_sched_barrier(0);
     m_phase(RoleB{}, SN{}, ST{});
     return t + 1 < nt;
   };
@@ -502,12 +505,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   if (nt > 0) {
     for (int i = 0; i < 4; ++i) issue_tile(i, i);
     sync_even(std::integral_constant<int, 4>{}, 0);
-    // Both roles pass the same 2*nt + 2 barriers.  The first product phase of
+    // Both roles pass the same nt + 2 barriers (one extra after the first step,
+    // which publishes the LSE of tiles 0 and 1).  The first product phase of
     // each role adds zeros times the resident tile 0, the last one computes the
     // score-like product of the reloaded last tile and drops it, so every
     // product phase is the same straight run of products.
     if (role == 0) {
       m_phase(RoleA{}, S0{}, S0{});
+      sync_plain();
       for (int t = 0;; t += 6) {
         if (!a_step(std::integral_constant<int, 0>{}, t)) break;
         if (!a_step(std::integral_constant<int, 1>{}, t + 1)) break;
@@ -516,10 +521,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
         if (!a_step(std::integral_constant<int, 4>{}, t + 4)) break;
         if (!a_step(std::integral_constant<int, 5>{}, t + 5)) break;
       }
-      sync_odd();
     } else {
       to_log2(S0{});
-      sync_odd();
+      to_log2(std::integral_constant<int, 1>{});
+      sync_plain();
       m_phase(RoleB{}, S0{}, S0{});
       for (int t = 0;; t += 6) {
         if (!b_step(std::integral_constant<int, 0>{}, t)) break;
@@ -562,8 +567,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 // dP^T = V dO^T (query on the lane axis, so each lane's LSE and Delta are one
 // value), P and dS = P (dP - Delta), then dQ^T += K^T dS^T with K^T read by the
 // LDS transpose read.  The products of tile t and the dQ product of tile t-1
-// form one phase, the P / dS arithmetic of tile t the next, and the two waves
-// of a SIMD run them one phase apart (the forward's ping-pong).
+// form one phase, the P / dS arithmetic of tile t another, and the two waves
+// of a SIMD run them in opposite orders between the barriers (the forward's
+// ping-pong).
 template <int D>
 struct DqCfg {
   static constexpr int NW = 8, BQ = 32 * NW, BK = 32, NT = 64 * NW, NST = 4;
@@ -790,20 +796,13 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
     for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(dqa[db]));
   };
 
-  // Phase boundaries, as in the forward: phase 2m starts once tile m is
-  // resident for every wave, and then the load of tile m+2 goes into the stage
-  // tile m-2 held (its last reader, a dQ product, ran in phase 2m-1).
+  // Step boundaries, as in the forward: step m starts once tile m is resident
+  // for every wave, and then the load of tile m+2 goes into the stage tile m-2
+  // held (its last readers, the dQ products of tile m-2, ran in step m-1).
   auto sync_even = [&](auto STAGE2, int m) {
     __builtin_amdgcn_sched_barrier(0);
     lds_ring_sync<LOADS_PER_TILE>();
     issue_tile(STAGE2, m + 2);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto sync_odd = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -817,56 +816,64 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
     issue_tile(S1{}, 1);
     sync_even(S2{}, 0);
     // Ping-pong between the two waves of each SIMD (waves w and w + NW/2), as in
-    // the forward: the first half runs the product phase of tile t in phase 2t
-    // and its arithmetic in phase 2t+1, the second half one phase later; both
-    // pass the same 2*nt + 2 barriers.
+    // the forward: in step t the first half runs the product phase of tile t,
+    // then its arithmetic; the second half the arithmetic of tile t-1, then the
+    // product phase of tile t; both pass the same nt + 1 barriers.
     if (w < Cfg::NW / 2) {
+      __builtin_amdgcn_sched_barrier(0);
       m_phase(S0{}, S0{});
       for (int t0 = 0;; t0 += 4) {
-        sync_odd();
         v_phase(t0);
+        __builtin_amdgcn_sched_barrier(0);
         sync_even(S3{}, t0 + 1);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S1{}, S0{});
         if (t0 + 1 == nt) break;
-        sync_odd();
         v_phase(t0 + 1);
+        __builtin_amdgcn_sched_barrier(0);
         sync_even(S0{}, t0 + 2);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S2{}, S1{});
         if (t0 + 2 == nt) break;
-        sync_odd();
         v_phase(t0 + 2);
+        __builtin_amdgcn_sched_barrier(0);
         sync_even(S1{}, t0 + 3);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S3{}, S2{});
         if (t0 + 3 == nt) break;
-        sync_odd();
         v_phase(t0 + 3);
+        __builtin_amdgcn_sched_barrier(0);
         sync_even(S2{}, t0 + 4);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S0{}, S3{});
         if (t0 + 4 == nt) break;
       }
-      sync_odd();
     } else {
-      sync_odd();
+      __builtin_amdgcn_sched_barrier(0);
       m_phase(S0{}, S0{});
       for (int t0 = 0;; t0 += 4) {
         sync_even(S3{}, t0 + 1);
         v_phase(t0);
-        sync_odd();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S1{}, S0{});
         if (t0 + 1 == nt) break;
         sync_even(S0{}, t0 + 2);
         v_phase(t0 + 1);
-        sync_odd();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S2{}, S1{});
         if (t0 + 2 == nt) break;
         sync_even(S1{}, t0 + 3);
         v_phase(t0 + 2);
-        sync_odd();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S3{}, S2{});
         if (t0 + 3 == nt) break;
         sync_even(S2{}, t0 + 4);
         v_phase(t0 + 3);
-        sync_odd();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S0{}, S3{});
         if (t0 + 4 == nt) break;
       }

@@ -11,8 +11,10 @@
 //  - Ping-pong between the two waves of each SIMD (waves w and w + 4): each
 //    tile takes a product phase (the scores of tile t and O += P V of tile t-1
 //    on the matrix cores) and a softmax phase (rescale, exponentials) on the
-//    vector ALU, and the two waves run them one phase apart, separated by
-//    workgroup barriers.  A wave that issues products and vector work in turn
+//    vector ALU.  Between two workgroup barriers (one per tile) the first-half
+//    wave runs product phase then softmax phase, the second-half wave softmax
+//    phase then product phase, so each tends to issue products while the other
+//    runs vector work.  A wave that issues products and vector work in turn
 //    stalls its vector work behind every product that waits for the matrix
 //    core; in the ping-pong one wave feeds the matrix core while the other
 //    keeps the vector ALU busy.  The product phase also takes the row sums of
@@ -391,22 +393,15 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
     pin_phase_outputs(st, oacc);
   };
 
-  // Phase boundaries.  Phase 2m starts once tile m is resident for every wave
-  // (each wave waits for its own loads of it, then the barrier), after which the
-  // load of tile m+2 goes out into the stage tile m-2 held: its last reader
-  // finished in phase 2m-1.  Odd phases start with a barrier alone.  The
-  // scheduling walls keep every instruction in its phase.
+  // Step boundaries.  Step m starts once tile m is resident for every wave (each
+  // wave waits for its own loads of it, then the barrier), after which the load
+  // of tile m+2 goes out into the stage tile m-2 held: its last readers (the O
+  // products of tile m-2) ran in step m-1.  The scheduling walls keep every
+  // instruction in its phase.
   auto sync_even = [&](auto STAGE2, int m) {
     __builtin_amdgcn_sched_barrier(0);
     lds_ring_sync<LOADS_PER_TILE>();
     issue_tile(STAGE2, m + 2);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto sync_odd = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -419,59 +414,69 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
     issue_tile(S0{}, 0);
     issue_tile(S1{}, 1);
     sync_even(S2{}, 0);
-    // Ping-pong: waves w and w + NW/2 share a SIMD.  The first half runs the
-    // product phase of tile t in phase 2t and the softmax of tile t in phase
-    // 2t+1; the second half runs one phase later.  So in every phase one wave of
-    // each SIMD issues only matrix-core products while the other runs only
-    // vector-ALU work, and the matrix cores never wait on a softmax.  Both halves
-    // pass the same 2*nt + 2 barriers.
+    // Ping-pong: waves w and w + NW/2 share a SIMD.  In step t the first half
+    // runs the product phase of tile t, then its softmax; the second half runs
+    // the softmax of tile t-1, then the product phase of tile t.  So one wave of
+    // each SIMD tends to issue products while the other runs vector work, and the
+    // product phase's issue priority keeps the matrix core fed where they
+    // overlap.  (A second barrier per tile that forced the phases apart cost
+    // more in waiting than it gained.)  Both halves pass the same nt + 1
+    // barriers.
     if (w < Cfg::NW / 2) {
+      __builtin_amdgcn_sched_barrier(0);
       m_phase(S0{}, S0{});
       for (int t0 = 0;; t0 += 4) {
-        sync_odd();
         v_phase(t0);
+        __builtin_amdgcn_sched_barrier(0);
         sync_even(S3{}, t0 + 1);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S1{}, S0{});
         if (t0 + 1 == nt) break;
-        sync_odd();
         v_phase(t0 + 1);
+        __builtin_amdgcn_sched_barrier(0);
         sync_even(S0{}, t0 + 2);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S2{}, S1{});
         if (t0 + 2 == nt) break;
-        sync_odd();
         v_phase(t0 + 2);
+        __builtin_amdgcn_sched_barrier(0);
         sync_even(S1{}, t0 + 3);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S3{}, S2{});
         if (t0 + 3 == nt) break;
-        sync_odd();
         v_phase(t0 + 3);
+        __builtin_amdgcn_sched_barrier(0);
         sync_even(S2{}, t0 + 4);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S0{}, S3{});
         if (t0 + 4 == nt) break;
       }
-      sync_odd();
     } else {
-      sync_odd();
+      __builtin_amdgcn_sched_barrier(0);
       m_phase(S0{}, S0{});
       for (int t0 = 0;; t0 += 4) {
         sync_even(S3{}, t0 + 1);
         v_phase(t0);
-        sync_odd();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S1{}, S0{});
         if (t0 + 1 == nt) break;
         sync_even(S0{}, t0 + 2);
         v_phase(t0 + 1);
-        sync_odd();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S2{}, S1{});
         if (t0 + 2 == nt) break;
         sync_even(S1{}, t0 + 3);
         v_phase(t0 + 2);
-        sync_odd();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S3{}, S2{});
         if (t0 + 3 == nt) break;
         sync_even(S2{}, t0 + 4);
         v_phase(t0 + 3);
-        sync_odd();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         m_phase(S0{}, S3{});
         if (t0 + 4 == nt) break;
       }
