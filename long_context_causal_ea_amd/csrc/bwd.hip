@@ -726,6 +726,7 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
   auto m_phase = [&](auto CSTAGE, auto PSTAGE) {
     constexpr int cst = decltype(CSTAGE)::value, pst = decltype(PSTAGE)::value;
     constexpr int NSD = 2 * NKS, NDQ = 2 * NDB, N = NSD + NDQ, PF = 3;
+    __builtin_amdgcn_s_setprio(2);  // the products win the issue port from the other wave's vector work
     constexpr int SUB_PER = (16 + NDQ - 3) / (NDQ - 2);  // Delta subtractions per dQ product (after the first two)
     static_assert(PF <= NSD, "the ring starts inside the score products");
     auto rd = [&](int i) {
@@ -771,6 +772,7 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
     asm volatile("" : "+v"(sc), "+v"(dpv));
 #pragma unroll
     for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(dqa[db]));
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Arithmetic phase of tile t: mask, P = exp2(S c - LSE2), dS = P (dP - Delta)
