@@ -656,29 +656,31 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
   // ---- direct global -> LDS loads (as in the forward); rows past the end of
   // the keys load the last key row, and the element mask removes them
   const int dma_row = lane / CPR, dma_slot = lane % CPR;
-  long dma_off[Cfg::NKL];
+  uint32_t dma_off[Cfg::NKL];  // byte offset from the tile's first row (a scalar base)
 #pragma unroll
   for (int it = 0; it < Cfg::NKL; ++it) {
     const int row = RPI * (w + Cfg::NW * it) + dma_row;
-    dma_off[it] = (long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3);
+    dma_off[it] = (uint32_t)(((long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
   }
   auto issue_tile = [&](auto STAGE, int t) {
     constexpr int stage = decltype(STAGE)::value;
     const int tt = t < nt ? t : nt - 1;  // past the end: reload the last tile into a stage nobody reads
-    const int j0 = tile_of(tt) * BK;
+    const int j0 = __builtin_amdgcn_readfirstlane(tile_of(tt) * BK);
     const bool whole = j0 + BK <= p.Sk;
+    const uint16_t* kb = kp + (long)j0 * p.rs;
+    const uint16_t* vb = vp + (long)j0 * p.rs;
 #pragma unroll
     for (int it = 0; it < Cfg::NKL; ++it) {
       if (Cfg::NLT < Cfg::NW && w >= Cfg::NLT) break;  // this wave loads nothing
       const int row0 = RPI * (w + Cfg::NW * it);
-      long off = (long)j0 * p.rs + dma_off[it];
+      uint32_t off = dma_off[it];
       if (!whole) {
         const int row = row0 + dma_row;
-        const int j = min(j0 + row, p.Sk - 1);
-        off = (long)j * p.rs + ((dma_slot ^ swz<D>(row)) << 3);
+        const int jj = min(row, p.Sk - 1 - j0);
+        off = (uint32_t)(((long)jj * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
       }
-      dma16(kp + off, &KV[stage][row0 * D]);
-      dma16(vp + off, &KV[stage][KT + row0 * D]);
+      dma16_s(kb, off, &KV[stage][row0 * D]);
+      dma16_s(vb, off, &KV[stage][KT + row0 * D]);
     }
   };
   constexpr int LOADS_PER_TILE = 2 * Cfg::NKL;

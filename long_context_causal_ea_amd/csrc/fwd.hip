@@ -190,29 +190,34 @@ __global__ __launch_bounds__(64 * EA_FWD_NW, FwdCfg<128>::MIN_WG) void fwd_kerne
   // 64 consecutive 16-byte LDS slots (RPI rows); lane i fills slot i % CPR of row
   // i / CPR, i.e. chunk (slot ^ swz(row)) of that row in the swizzled layout.
   const int dma_row = lane / CPR, dma_slot = lane % CPR;
-  long dma_off[Cfg::NKL];  // element offset of this lane's 16 bytes within a tile whose first row is 0
+  // byte offset of this lane's 16 bytes from the first row of a tile (a tile spans
+  // BK rows of H*D elements, so it fits in 32 bits); the tile's first row is a
+  // scalar base
+  uint32_t dma_off[Cfg::NKL];
 #pragma unroll
   for (int it = 0; it < Cfg::NKL; ++it) {
     const int row = RPI * (w + Cfg::NW * it) + dma_row;
-    dma_off[it] = (long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3);
+    dma_off[it] = (uint32_t)(((long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
   }
   auto issue_tile = [&](auto STAGE, int t) {
     constexpr int stage = decltype(STAGE)::value;
     const int tt = t < nt ? t : nt - 1;  // past the end: reload the last tile into a stage nobody reads
-    const int j0 = tile_of(tt) * BK;
+    const int j0 = __builtin_amdgcn_readfirstlane(tile_of(tt) * BK);
     const bool whole = j0 + BK <= p.Sk;
+    const uint16_t* kb = kp + (long)j0 * p.rs;
+    const uint16_t* vb = vp + (long)j0 * p.rs;
 #pragma unroll
     for (int it = 0; it < Cfg::NKL; ++it) {
       if (Cfg::NLT < Cfg::NW && w >= Cfg::NLT) break;  // this wave loads nothing (its vmcnt waits pass at once)
       const int row0 = RPI * (w + Cfg::NW * it);
-      long off = (long)j0 * p.rs + dma_off[it];
+      uint32_t off = dma_off[it];
       if (!whole) {
         const int row = row0 + dma_row;
-        const int j = min(j0 + row, p.Sk - 1);
-        off = (long)j * p.rs + ((dma_slot ^ swz<D>(row)) << 3);
+        const int jj = min(row, p.Sk - 1 - j0);
+        off = (uint32_t)(((long)jj * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
       }
-      dma16(kp + off, &Ks[stage][row0 * D]);
-      dma16(vp + off, &Vs[stage][row0 * D]);
+      dma16_s(kb, off, &Ks[stage][row0 * D]);
+      dma16_s(vb, off, &Vs[stage][row0 * D]);
     }
   };
   constexpr int LOADS_PER_TILE = 2 * Cfg::NKL;
