@@ -331,6 +331,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   // So one wave of each SIMD tends to feed the matrix core while the other runs
   // vector work.  (A second barrier per step that forced the phases apart cost
   // more in waiting than it gained.)
+  f32x4 lsepf[4];                        // A: base-2 LSE of the tile's rows, read in the product phase
   f32x16 sx;                             // A: S of the current tile; B: dP
   bf16x8 pk[2] = {bf16x8{}, bf16x8{}};   // A: P of the previous tile; B: dS of the previous tile (bf16)
 
@@ -354,6 +355,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     u32x4 fr[N];
 #pragma unroll
     for (int i = 0; i < PF; ++i) fr[i] = rd(i);
+    if constexpr (R == 0) {  // the new tile's LSE (converted in the previous step) for the vector phase
+      const f32x4* lsrc = reinterpret_cast<const f32x4*>(&Ss[cst][4 * g]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) lsepf[m] = lsrc[2 * m];
+    }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       if (i + PF < N) fr[i + PF] = rd(i + PF);
@@ -373,8 +379,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
       } else if (i + PF < N) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two reads of product i + PF
       }
+      if (R == 0 && i == 1) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the LSE reads
     }
     asm volatile("" : "+v"(sx));
+    if constexpr (R == 0) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) asm volatile("" : "+v"(lsepf[m]));
+    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(acc[db]));
   };
@@ -391,7 +402,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   };
 
   // A's vector phase for tile t (stage st): mask, P = exp2(S c - LSE2) (the LSE
-  // of the tile's rows is already in base-2 units, see to_log2), published to
+  // of the tile's rows, already in base-2 units (see to_log2), was read in the
+  // product phase of the same step), published to
   // B as fp16 pairs, kept as bf16 packs for dV.  A barrier does not wait for
   // memory, so A waits for its LDS writes before the barrier that publishes them.
   auto a_v = [&](auto ST, int t) {
@@ -406,7 +418,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     }
     float pv[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(sx[r], c, -Ss[st][8 * (r >> 2) + 4 * g + (r & 3)]));
+    for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(sx[r], c, -lsepf[r >> 2][r & 3]));
     uint32_t* pdst = &Ps[t & 1][kw][0][lane][0];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -454,6 +466,16 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     }
     if (w == 4) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
+  // the same in two parts around B's vector phase, so that the read's latency hides under it
+  auto lse_read = [&](auto ST) {
+    constexpr int stage = decltype(ST)::value;
+    return (w == 4 && g == 0) ? Ss[stage][ln] : 0.f;
+  };
+  auto lse_write = [&](auto ST, float l) {
+    constexpr int stage = decltype(ST)::value;
+    if (w == 4 && g == 0) Ss[stage][ln] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e - kPScaleLog2;
+    if (w == 4) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
 
   // Step m starts once tiles m and m+1 are resident for every wave (tile m+1
   // for the LSE conversion); then the loads of tile m+4 go into the stage tile
@@ -495,8 +517,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     using SL = std::integral_constant<int, (u + 5) % NST>;
     using SNN = std::integral_constant<int, (u + 2) % NST>;
     sync_even(SL{}, t + 1);
+    const float lraw = lse_read(SNN{});
     b_v(ST{}, t);
-    to_log2(SNN{});
+    lse_write(SNN{}, lraw);
     __builtin_amdgcn_sched_barrier(0);
     m_phase(RoleB{}, SN{}, ST{});
     return t + 1 < nt;
@@ -513,6 +536,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     if (role == 0) {
       m_phase(RoleA{}, S0{}, S0{});
       sync_plain();
+      {  // tile 0's LSE is converted before this barrier, after the first product phase read it
+        const f32x4* lsrc = reinterpret_cast<const f32x4*>(&Ss[0][4 * g]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) lsepf[m] = lsrc[2 * m];
+      }
       for (int t = 0;; t += 6) {
         if (!a_step(std::integral_constant<int, 0>{}, t)) break;
         if (!a_step(std::integral_constant<int, 1>{}, t + 1)) break;
