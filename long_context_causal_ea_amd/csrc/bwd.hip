@@ -167,7 +167,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   constexpr int OT = Cfg::LDS_T;
   // stage s: Q tile at QO[s][0], dO tile at QO[s][OT]
   __shared__ __attribute__((aligned(16))) uint16_t QO[NST][2 * OT];
-  __shared__ __attribute__((aligned(16))) float Ss[NST][2 * BQ];  // LSE of the rows, then Delta
+  // LSE of the rows, then Delta.  The largest alignment places it first in LDS,
+  // so its accesses take the 16-bit immediate offset of the LDS instructions
+  // (behind the 112 KB of tiles each access needed an address add: 0.6 ms of
+  // the pass at 64K tokens)
+  __shared__ __attribute__((aligned(1024))) float Ss[NST][2 * BQ];
   // P of the last two tiles per key group, fp16 pairs: [slot][group][half of the 16 values][lane][pair]
   __shared__ __attribute__((aligned(16))) uint32_t Ps[2][4][2][64][4];
 
