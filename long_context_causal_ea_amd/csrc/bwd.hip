@@ -257,7 +257,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   // ---- direct global -> LDS loads: load k of a tile (k = w + NW*i) moves rows
   // [RPI*(k % (NI/2)), +RPI) of Q (k < NI/2) or dO; lane i fills 16-byte slot
   // i % CPR of row i / CPR, i.e. chunk slot ^ swz(row).  Wave 0 also moves the
-  // 32 LSE and 32 Delta values of the tile (4 bytes per lane).
+  // tile's 32 LSE and 32 Delta values (4 bytes per lane, lane i to word i).
+  // (Spreading that load over the eight waves, eight lanes each, so that every
+  // wave waits for the same count, cost 2.6 ms at 64K tokens: each wave then
+  // waits for a scattered load of its own.)
   const int dma_row = lane / CPR, dma_slot = lane % CPR;
   uint32_t dma_off[Cfg::NIW];
 #pragma unroll
@@ -267,35 +270,73 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     dma_off[i] = (uint32_t)(((long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
   }
   const float* stat_src = g == 0 ? lsep : delp;  // lanes 0..31: LSE, 32..63: Delta
-  auto issue_tile = [&](int stage, int t) {
-    const int tt = t < nt ? t : nt - 1;  // past the end: reload the last tile into a stage nobody reads
-    const int i0 = __builtin_amdgcn_readfirstlane(tile_of(tt) * BQ);
-    const bool whole = i0 + BQ <= p.Sq;
+  const float* stat_lane = stat_src + (long)ln * p.Hs;
+  const bool stat_mine = w == 0;  // uniform per wave
+  auto load_rows = [&](int stage, const uint16_t* qt, const uint16_t* ot, const float* st) {
 #pragma unroll
     for (int i = 0; i < Cfg::NIW; ++i) {
       const int k = w + Cfg::NW * i, tns = k / (Cfg::NI / 2), part = k % (Cfg::NI / 2);
-      const int row0 = RPI * part;
-      uint32_t off = dma_off[i];
-      if (!whole) {  // rows past the end load the last row; the element mask removes them
-        const int row = row0 + dma_row;
-        const int ii = min(row, p.Sq - 1 - i0);
-        off = (uint32_t)(((long)ii * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
-      }
-      dma16_s((tns ? op : qp) + (long)i0 * p.rs, off, &QO[stage][tns * OT + row0 * D]);
+      dma16_s(tns ? ot : qt, dma_off[i], &QO[stage][tns * OT + RPI * part * D]);
     }
-    if (w == 0) dma4(stat_src + (long)min(i0 + ln, p.Sq - 1) * p.Hs, &Ss[stage][0]);
+    if (stat_mine) dma4(st, &Ss[stage][0]);
   };
-  constexpr int LOADS = Cfg::NIW;  // per tile for waves 1..7 (wave 0: one more)
-
-  auto wait_ring = [&](auto N) {  // this wave's loads of the tiles up to the one needed have landed; barrier
+  // Any tile t (prologue): t past the last tile reloads the last one into a
+  // stage nobody reads; rows past the end of the queries load the last row
+  // (the element mask removes them).  Only the first tile visited can be such
+  // a ragged tile: it is the highest tile of the last segment visited first.
+  auto issue_any = [&](int stage, int t) {
+    const int tt = t < nt ? t : nt - 1;
+    const int i0 = __builtin_amdgcn_readfirstlane(tile_of(tt) * BQ);
+    const uint16_t* qt = qp + (long)i0 * p.rs;
+    const uint16_t* ot = op + (long)i0 * p.rs;
+    if (i0 + BQ <= p.Sq) {
+      load_rows(stage, qt, ot, stat_lane + (long)i0 * p.Hs);
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::NIW; ++i) {
+      const int k = w + Cfg::NW * i, tns = k / (Cfg::NI / 2), part = k % (Cfg::NI / 2);
+      const int row0 = RPI * part, row = row0 + dma_row;
+      const int ii = min(row, p.Sq - 1 - i0);
+      const uint32_t off = (uint32_t)(((long)ii * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
+      dma16_s(tns ? ot : qt, off, &QO[stage][tns * OT + row0 * D]);
+    }
+    if (stat_mine) dma4(stat_src + (long)min(i0 + ln, p.Sq - 1) * p.Hs, &Ss[stage][0]);
+  };
+  // Tiles 5, 6, ... (whole, before the last): scalar pointers to the first row
+  // of the next tile, stepped down one tile per load, except once, from the
+  // lowest tile of the segment visited first over the causally skipped tiles
+  // to the highest tile of the other (a longer step).
+  const long tstep = (long)BQ * p.rs;
+  const long jstep = (long)(tC0 - tA1 + 1) * BQ * p.rs;
+  const int sstep = BQ * p.Hs, sjump = (tC0 - tA1 + 1) * BQ * p.Hs;
+  const uint16_t* nq = qp;
+  const uint16_t* no = op;
+  int ns = 0;  // statistics: first row times Hs
+  {
+    const int r5 = __builtin_amdgcn_readfirstlane(tile_of(5 < nt ? 5 : 0) * BQ);
+    nq += (long)r5 * p.rs;
+    no += (long)r5 * p.rs;
+    ns = r5 * p.Hs;
+  }
+  auto issue_next = [&](int stage, int m) {  // loads tile m + 4 (>= 5, < nt), then points at tile m + 5
+    load_rows(stage, nq, no, stat_lane + ns);
+    const bool jump = m + 5 == nC;
+    const long st = jump ? jstep : tstep;
+    nq -= st;
+    no -= st;
+    ns -= jump ? sjump : sstep;
+  };
+  constexpr int LOADS = Cfg::NIW;  // per tile and wave (wave 0: one more)
+  // this wave's loads of all but the last N tiles it issued have landed
+  auto wait_loads = [&](auto N) {
     constexpr int n = decltype(N)::value;
     if (w == 0)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n * (LOADS + 1)) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n * LOADS) : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
   };
+
   // per-lane LDS offsets (elements)
   // operand of the score products: row ln, chunk 2*ks+g = slot 2*(ks ^ qx) + (g ^ (swz & 1))
   const int qx = swz<D>(ln) >> 1, qbase = ln * D + ((g ^ (swz<D>(ln) & 1)) << 3);
@@ -487,10 +528,19 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   // m-1).
   constexpr int AHEAD = 2;  // tiles in flight beyond the two needed
   static_assert(NST == 6, "loads run four tiles ahead in a ring of six stages");
+  // Near the end no tile is loaded and the wave waits for all of its loads.
   auto sync_even = [&](auto STAGE4, int m) {
     __builtin_amdgcn_sched_barrier(0);
-    wait_ring(std::integral_constant<int, AHEAD>{});
-    issue_tile(decltype(STAGE4)::value, m + 4);
+    if (m + 4 < nt) {
+      wait_loads(std::integral_constant<int, AHEAD>{});
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue_next(decltype(STAGE4)::value, m);
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   auto sync_plain = [&]() {
@@ -530,13 +580,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   };
 
   if (nt > 0) {
-    for (int i = 0; i < 4; ++i) issue_tile(i, i);
-    sync_even(std::integral_constant<int, 4>{}, 0);
+    for (int i = 0; i < 4; ++i) issue_any(i, i);
+    wait_loads(std::integral_constant<int, AHEAD>{});
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue_any(4, 4);
     // Both roles pass the same nt + 2 barriers (one extra after the first step,
     // which publishes the LSE of tiles 0 and 1).  The first product phase of
     // each role adds zeros times the resident tile 0, the last one computes the
-    // score-like product of the reloaded last tile and drops it, so every
-    // product phase is the same straight run of products.
+    // score-like product of a stage that holds no new tile (an older or a
+    // reloaded one) and drops it, so every product phase is the same straight
+    // run of products.
     if (role == 0) {
       m_phase(RoleA{}, S0{}, S0{});
       sync_plain();
