@@ -748,26 +748,55 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
     const int row = RPI * (w + Cfg::NW * it) + dma_row;
     dma_off[it] = (uint32_t)(((long)row * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
   }
-  auto issue_tile = [&](auto STAGE, int t) {
+  auto load_kv = [&](auto STAGE, const uint16_t* kb, const uint16_t* vb) {
     constexpr int stage = decltype(STAGE)::value;
-    const int tt = t < nt ? t : nt - 1;  // past the end: reload the last tile into a stage nobody reads
-    const int j0 = __builtin_amdgcn_readfirstlane(tile_of(tt) * BK);
-    const bool whole = j0 + BK <= p.Sk;
-    const uint16_t* kb = kp + (long)j0 * p.rs;
-    const uint16_t* vb = vp + (long)j0 * p.rs;
 #pragma unroll
     for (int it = 0; it < Cfg::NKL; ++it) {
       if (Cfg::NLT < Cfg::NW && w >= Cfg::NLT) break;  // this wave loads nothing
       const int row0 = RPI * (w + Cfg::NW * it);
-      uint32_t off = dma_off[it];
-      if (!whole) {
-        const int row = row0 + dma_row;
-        const int jj = min(row, p.Sk - 1 - j0);
-        off = (uint32_t)(((long)jj * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
-      }
+      dma16_s(kb, dma_off[it], &KV[stage][row0 * D]);
+      dma16_s(vb, dma_off[it], &KV[stage][KT + row0 * D]);
+    }
+  };
+  // Any tile t (prologue, and a ragged last tile): t past the last tile reloads
+  // it into a stage nobody reads.  Only the last tile visited, the highest, can
+  // be ragged.
+  auto issue_any = [&](auto STAGE, int t) {
+    constexpr int stage = decltype(STAGE)::value;
+    const int tt = t < nt ? t : nt - 1;
+    const int j0 = __builtin_amdgcn_readfirstlane(tile_of(tt) * BK);
+    const uint16_t* kb = kp + (long)j0 * p.rs;
+    const uint16_t* vb = vp + (long)j0 * p.rs;
+    if (j0 + BK <= p.Sk) {
+      load_kv(STAGE, kb, vb);
+      return;
+    }
+#pragma unroll
+    for (int it = 0; it < Cfg::NKL; ++it) {
+      if (Cfg::NLT < Cfg::NW && w >= Cfg::NLT) break;
+      const int row0 = RPI * (w + Cfg::NW * it), row = row0 + dma_row;
+      const int jj = min(row, p.Sk - 1 - j0);
+      const uint32_t off = (uint32_t)(((long)jj * p.rs + ((dma_slot ^ swz<D>(row)) << 3)) * 2);
       dma16_s(kb, off, &KV[stage][row0 * D]);
       dma16_s(vb, off, &KV[stage][KT + row0 * D]);
     }
+  };
+  // Tiles 2 .. nfast-1 (whole): scalar pointers stepped up one tile per load,
+  // except once, over the causally skipped tiles between the two runs.
+  const int nfast = nt > 0 && tile_of(nt - 1) * BK + BK > p.Sk ? nt - 1 : nt;
+  const long kstep = (long)BK * p.rs, kjump = (long)(tB0 - nA + 1) * BK * p.rs;
+  const uint16_t* nk = kp;
+  const uint16_t* nv = vp;
+  {
+    const int r2 = __builtin_amdgcn_readfirstlane(tile_of(2 < nt ? 2 : 0) * BK);
+    nk += (long)r2 * p.rs;
+    nv += (long)r2 * p.rs;
+  }
+  auto issue_next = [&](auto STAGE, int m) {  // loads tile m + 2 (>= 2, < nfast), then points at tile m + 3
+    load_kv(STAGE, nk, nv);
+    const long st = m + 3 == nA ? kjump : kstep;
+    nk += st;
+    nv += st;
   };
   constexpr int LOADS_PER_TILE = 2 * Cfg::NKL;
 
@@ -808,8 +837,8 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
   // (k-step major), then dQ^T += K^T(t-1) dS^T(t-1) with K^T read transposed
   // from stage PSTAGE.  Between the dQ products the wave subtracts Delta from
   // the landed dP.  The first phase (t = 0) adds dS = 0 times the resident tile
-  // 0; the last (t = nt) computes the products of the reloaded last tile and
-  // drops them.  Operands go through a register ring PF products deep, pinned by
+  // 0; the last (t = nt) computes the products of a stage holding no new tile
+  // and drops them.  Operands go through a register ring PF products deep, pinned by
   // scheduling groups (as in the forward).
   auto m_phase = [&](auto CSTAGE, auto PSTAGE) {
     constexpr int cst = decltype(CSTAGE)::value, pst = decltype(PSTAGE)::value;
@@ -889,10 +918,16 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
   // Step boundaries, as in the forward: step m starts once tile m is resident
   // for every wave, and then the load of tile m+2 goes into the stage tile m-2
   // held (its last readers, the dQ products of tile m-2, ran in step m-1).
+  // Near the end (and before a ragged last tile) the wave waits for all of its loads.
   auto sync_even = [&](auto STAGE2, int m) {
     __builtin_amdgcn_sched_barrier(0);
-    lds_ring_sync<LOADS_PER_TILE>();
-    issue_tile(STAGE2, m + 2);
+    if (m + 2 < nfast) {
+      lds_ring_sync<LOADS_PER_TILE>();
+      issue_next(STAGE2, m);
+    } else {
+      lds_ring_sync<0>();
+      if (m + 2 < nt) issue_any(STAGE2, m + 2);
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -902,8 +937,8 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
-    issue_tile(S0{}, 0);
-    issue_tile(S1{}, 1);
+    issue_any(S0{}, 0);
+    issue_any(S1{}, 1);
     sync_even(S2{}, 0);
     // Ping-pong between the two waves of each SIMD (waves w and w + NW/2), as in
     // the forward: in step t the first half runs the product phase of tile t,
