@@ -91,6 +91,11 @@ CASES = [
     # positions at the top of the range (every position < 2^31)
     (128, 1, 300, 400, True, [2 ** 31 - 300, 300], [2 ** 31 - 500, 400], torch.float32),
     (64, 1, 200, 200, True, [2 ** 31 - 200, 100, 1000, 100], [2 ** 31 - 150, 150, 0, 50], torch.float32),
+    # second segment before the first, so that the causal rule skips whole tiles between the two runs a
+    # workgroup visits, far enough into its run for the loads to step over them: query tiles in dK/dV
+    # (ragged Sq), key tiles in the forward and dQ (ragged Sk)
+    (128, 1, 700, 600, True, [1000, 300, 0, 400], [0, 600], torch.float32),
+    (128, 1, 1200, 700, True, [0, 1200], [1000, 400, 0, 300], torch.float32),
 ]
 
 
