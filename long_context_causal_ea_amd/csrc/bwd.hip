@@ -489,8 +489,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * m + e;
-        const float pr = unpack_f16(ph[r >> 3][(r & 7) >> 1], r & 1);
-        dsv[r] = pr * (sx[r] - dm[e]);
+        dsv[r] = mul_f16_f32(ph[r >> 3][(r & 7) >> 1], r & 1, sx[r] - dm[e]);
       }
     }
     pack16(dsv);

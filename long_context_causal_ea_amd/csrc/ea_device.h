@@ -54,9 +54,18 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
-// Half `hi` (0: low, 1: high) of a packed fp16 pair, exactly as fp32.
-__device__ __forceinline__ float unpack_f16(uint32_t u, int hi) {
-  return (float)__builtin_bit_cast(f16x2, u)[hi];
+// Half `hi` (0: low, 1: high) of a packed fp16 pair, widened to fp32 (exact),
+// times b, in one instruction: the mixed-precision FMA takes the fp16 half as
+// it is and adds -0, which leaves every product, the sign of a zero one
+// included, as the fp32 multiply rounds it.  (The compiler does not form it
+// from a conversion and a multiply.)
+__device__ __forceinline__ float mul_f16_f32(uint32_t u, int hi, float b) {
+  float y;
+  if (hi)
+    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(y) : "v"(u), "v"(b), "v"(0.0f));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(y) : "v"(u), "v"(b), "v"(0.0f));
+  return y;
 }
 
 __device__ __forceinline__ bf16x8 pack_bf16x8(float x0, float x1, float x2, float x3, float x4, float x5,
