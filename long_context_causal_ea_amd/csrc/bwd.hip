@@ -376,7 +376,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   // So one wave of each SIMD tends to feed the matrix core while the other runs
   // vector work.  (A second barrier per step that forced the phases apart cost
   // more in waiting than it gained.)
-  f32x4 lsepf[4];                        // A: base-2 LSE of the tile's rows, read in the product phase
+  f32x4 lsepf[4];  // A: base-2 LSE of the tile's rows, read in the product phase; B: -Delta of the next tile's
+                   // rows, read in the vector phase, the start of the next dP accumulation
   f32x16 sx;                             // A: S of the current tile; B: dP
   bf16x8 pk[2] = {bf16x8{}, bf16x8{}};   // A: P of the previous tile; B: dS of the previous tile (bf16)
 
@@ -409,7 +410,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     for (int i = 0; i < N; ++i) {
       if (i + PF < N) fr[i + PF] = rd(i + PF);
       if (i < NSC) {
-        sx = mfma32(as_bf16x8(fr[i]), kvf[i], i == 0 ? f32x16{} : sx);
+        f32x16 c0 = f32x16{};  // B: dP - Delta comes out of the products (register r holds row 8(r/4)+4g+r%4)
+        if constexpr (R == 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c0[r] = lsepf[r >> 2][r & 3];
+        }
+        sx = mfma32(as_bf16x8(fr[i]), kvf[i], i == 0 ? c0 : sx);
       } else {
         const int j = i - NSC;
         acc[j % NDB] = mfma32(as_bf16x8(fr[i]), pk[j / NDB], acc[j % NDB]);
@@ -476,48 +482,44 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
-  // B's vector phase for tile t (stage st): dS = P (dP - Delta) from A's P(t).
-  auto b_v = [&](auto ST, int t) {
-    constexpr int st = decltype(ST)::value;
+  // B's vector phase for tile t (stage st): dS = P (dP - Delta) from A's P(t)
+  // (its product phase started the dP accumulation from -Delta).
+  auto b_v = [&](auto, int t) {
     const u32x4* psrc8 = reinterpret_cast<const u32x4*>(&Ps[t & 1][kw][0][lane][0]);
-    const f32x4* dsrc4 = reinterpret_cast<const f32x4*>(&Ss[st][BQ + 4 * g]);
     const u32x4 ph[2] = {psrc8[0], psrc8[64]};
     float dsv[16];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const f32x4 dm = dsrc4[2 * m];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * m + e;
-        dsv[r] = mul_f16_f32(ph[r >> 3][(r & 7) >> 1], r & 1, sx[r] - dm[e]);
-      }
-    }
+    for (int r = 0; r < 16; ++r) dsv[r] = mul_f16_f32(ph[r >> 3][(r & 7) >> 1], r & 1, sx[r]);
     pack16(dsv);
     asm volatile("" : "+v"(sx));
   };
 
-  // Wave 4 (a V-side wave) rewrites the LSE of tile t+1 in base-2 units less
-  // kPScaleLog2 during step t, after its vector phase, so that exp2 gives
-  // 2^kPScaleLog2 P (-inf, a row without any allowed key, becomes +inf so that
-  // its recomputed probabilities are exactly 0); the next barrier publishes the
-  // converted values before A's vector phase of step t+1 reads them (wave 4
-  // waits for its write first: a barrier does not wait for memory).
+  // Wave 4 (a V-side wave) rewrites the row statistics of tile t+1 during step
+  // t, after its vector phase: lanes 0..31 the LSE in base-2 units less
+  // kPScaleLog2, so that exp2 gives 2^kPScaleLog2 P (-inf, a row without any
+  // allowed key, becomes +inf so that its recomputed probabilities are exactly
+  // 0), lanes 32..63 Delta negated (the start of the dP accumulations); the next
+  // barrier publishes the converted values before they are read in step t+1
+  // (wave 4 waits for its write first: a barrier does not wait for memory).
+  auto stat_conv = [&](float l) {
+    return g == 1 ? -l : (l == -__builtin_inff() ? __builtin_inff() : l * kLog2e - kPScaleLog2);
+  };
   auto to_log2 = [&](auto ST) {
     constexpr int stage = decltype(ST)::value;
-    if (w == 4 && g == 0) {
-      const float l = Ss[stage][ln];
-      Ss[stage][ln] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e - kPScaleLog2;
+    if (w == 4) {
+      const float l = Ss[stage][lane];
+      Ss[stage][lane] = stat_conv(l);
     }
     if (w == 4) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
   // the same in two parts around B's vector phase, so that the read's latency hides under it
   auto lse_read = [&](auto ST) {
     constexpr int stage = decltype(ST)::value;
-    return (w == 4 && g == 0) ? Ss[stage][ln] : 0.f;
+    return w == 4 ? Ss[stage][lane] : 0.f;
   };
   auto lse_write = [&](auto ST, float l) {
     constexpr int stage = decltype(ST)::value;
-    if (w == 4 && g == 0) Ss[stage][ln] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e - kPScaleLog2;
+    if (w == 4) Ss[stage][lane] = stat_conv(l);
     if (w == 4) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
@@ -571,6 +573,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     using SNN = std::integral_constant<int, (u + 2) % NST>;
     sync_even(SL{}, t + 1);
     const float lraw = lse_read(SNN{});
+    {  // -Delta of tile t+1 (negated in step t-1) for the next product phase
+      const f32x4* dsrc = reinterpret_cast<const f32x4*>(&Ss[SN::value][BQ + 4 * g]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) lsepf[m] = dsrc[2 * m];
+    }
     b_v(ST{}, t);
     lse_write(SNN{}, lraw);
     __builtin_amdgcn_sched_barrier(0);
@@ -610,6 +617,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
       to_log2(S0{});
       to_log2(std::integral_constant<int, 1>{});
       sync_plain();
+      {
+        const f32x4* dsrc = reinterpret_cast<const f32x4*>(&Ss[0][BQ + 4 * g]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) lsepf[m] = dsrc[2 * m];
+      }
       m_phase(RoleB{}, S0{}, S0{});
       for (int t = 0;; t += 6) {
         if (!b_step(std::integral_constant<int, 0>{}, t)) break;
@@ -713,6 +725,9 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
   for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qf[ks]), "+v"(of[ks]));
   float l2 = lse2, dl = dlt;
   asm volatile("" : "+v"(l2), "+v"(dl));
+  f32x16 negd;  // -Delta of the lane's row: the start of every dP^T accumulation, so dP^T - Delta comes out of it
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = -dl;
   const int qpos = seg_pos(p.qs, row_ok ? qrow : (p.Sq - 1));
   const KeyWindow kwin = key_window(p.ks, qpos, p.causal);
 
@@ -832,18 +847,17 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
                    // register r of lane l holds key 8*(r/4) + 4*g + r%4 of query ln
   bf16x8 sb[2] = {bf16x8{}, bf16x8{}};  // dS^T of the previous tile, keys 0-15 and 16-31, as B operands
 
-  // Product phase of tile t: S^T(t) = K Q^T and dP^T(t) = V dO^T from stage CSTAGE
-  // (k-step major), then dQ^T += K^T(t-1) dS^T(t-1) with K^T read transposed
-  // from stage PSTAGE.  Between the dQ products the wave subtracts Delta from
-  // the landed dP.  The first phase (t = 0) adds dS = 0 times the resident tile
-  // 0; the last (t = nt) computes the products of a stage holding no new tile
-  // and drops them.  Operands go through a register ring PF products deep, pinned by
-  // scheduling groups (as in the forward).
+  // Product phase of tile t: S^T(t) = K Q^T and dP^T(t) = V dO^T from stage
+  // CSTAGE (k-step major; the dP^T accumulation starts from -Delta), then
+  // dQ^T += K^T(t-1) dS^T(t-1) with K^T read transposed from stage PSTAGE.  The
+  // first phase (t = 0) adds dS = 0 times the resident tile 0; the last (t = nt)
+  // computes the products of a stage holding no new tile and drops them.
+  // Operands go through a register ring PF products deep, pinned by scheduling
+  // groups (as in the forward).
   auto m_phase = [&](auto CSTAGE, auto PSTAGE) {
     constexpr int cst = decltype(CSTAGE)::value, pst = decltype(PSTAGE)::value;
     constexpr int NSD = 2 * NKS, NDQ = 2 * NDB, N = NSD + NDQ, PF = 3;
     __builtin_amdgcn_s_setprio(2);  // the products win the issue port from the other wave's vector work
-    constexpr int SUB_PER = (16 + NDQ - 3) / (NDQ - 2);  // Delta subtractions per dQ product (after the first two)
     static_assert(PF <= NSD, "the ring starts inside the score products");
     auto rd = [&](int i) {
       if (i < NSD) {  // K (even i) or V (odd i) operand of k-step i / 2
@@ -864,7 +878,7 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
       if (i < NSD) {
         const int ks = i >> 1;
         if (i & 1)
-          dpv = mfma32(as_bf16x8(fr[i]), of[ks], ks == 0 ? f32x16{} : dpv);
+          dpv = mfma32(as_bf16x8(fr[i]), of[ks], ks == 0 ? negd : dpv);
         else
           sc = mfma32(as_bf16x8(fr[i]), qf[ks], ks == 0 ? f32x16{} : sc);
       } else {
@@ -872,8 +886,6 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
         dqa[j % NDB] = mfma32(as_bf16x8(fr[i]), sb[j / NDB], dqa[j % NDB]);
       }
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dpv[r] -= dl;
     __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // operands of the first PF products
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -883,7 +895,6 @@ __global__ __launch_bounds__(64 * DqCfg<128>::NW, 1) void dq_kernel(BwdParams p)
       } else if (i + PF < N) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two reads of dQ product i + PF - NSD
       }
-      if (i >= NSD + 2) __builtin_amdgcn_sched_group_barrier(0x002, SUB_PER, 0);  // Delta subtractions
     }
     asm volatile("" : "+v"(sc), "+v"(dpv));
 #pragma unroll
