@@ -468,15 +468,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
       }
     }
     float pv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(sx[r], c, -lsepf[r >> 2][r & 3]));
     uint32_t* pdst = &Ps[t & 1][kw][0][lane][0];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 2; ++j) {  // each half is written as soon as it is formed (the wall keeps it so), so
+                                   // the first write's latency passes under the second half's exponentials
+#pragma unroll
+      for (int r = 8 * j; r < 8 * j + 8; ++r) pv[r] = fast_exp2(__builtin_fmaf(sx[r], c, -lsepf[r >> 2][r & 3]));
       u32x4 hv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) hv[e] = pack_f16x2(pv[8 * j + 2 * e], pv[8 * j + 2 * e + 1]);
       *reinterpret_cast<u32x4*>(pdst + j * 256) = hv;
+      __builtin_amdgcn_sched_barrier(0);
     }
     pack16(pv);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
