@@ -484,18 +484,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
-  // B's vector phase for tile t (stage st): dS = P (dP - Delta) from A's P(t)
-  // (its product phase started the dP accumulation from -Delta).
-  auto b_v = [&](auto, int t) {
-    const u32x4* psrc8 = reinterpret_cast<const u32x4*>(&Ps[t & 1][kw][0][lane][0]);
-    const u32x4 ph[2] = {psrc8[0], psrc8[64]};
-    float dsv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dsv[r] = mul_f16_f32(ph[r >> 3][(r & 7) >> 1], r & 1, sx[r]);
-    pack16(dsv);
-    asm volatile("" : "+v"(sx));
-  };
-
   // Wave 4 (a V-side wave) rewrites the row statistics of tile t+1 during step
   // t, after its vector phase: lanes 0..31 the LSE in base-2 units less
   // kPScaleLog2, so that exp2 gives 2^kPScaleLog2 P (-inf, a row without any
@@ -514,7 +502,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     }
     if (w == 4) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  // the same in two parts around B's vector phase, so that the read's latency hides under it
+  // the same in two parts around B's vector phase, so that the read's latency hides under it (B's
+  // vector phase issues the read)
   auto lse_read = [&](auto ST) {
     constexpr int stage = decltype(ST)::value;
     return w == 4 ? Ss[stage][lane] : 0.f;
@@ -523,6 +512,31 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     constexpr int stage = decltype(ST)::value;
     if (w == 4) Ss[stage][lane] = stat_conv(l);
     if (w == 4) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
+  // B's vector phase for tile t: dS = P (dP - Delta) from A's P(t) (its product
+  // phase started the dP accumulation from -Delta).  It reads P(t) first, then
+  // -Delta of tile t+1 (stage SN, negated one step earlier) for the next
+  // product phase and, on wave 4, the raw statistic of tile t+2 (stage SNN)
+  // that it converts afterwards (returned); the reads return in that order.
+  auto b_v = [&](auto SN, auto SNN, int t) {
+    const u32x4* psrc8 = reinterpret_cast<const u32x4*>(&Ps[t & 1][kw][0][lane][0]);
+    u32x4 ph[2];
+    ph[0] = psrc8[0];
+    ph[1] = psrc8[64];
+    {
+      const f32x4* dsrc = reinterpret_cast<const f32x4*>(&Ss[decltype(SN)::value][BQ + 4 * g]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) lsepf[m] = dsrc[2 * m];
+    }
+    const float lraw = lse_read(SNN);
+    __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);  // the seven reads in program order
+    float dsv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dsv[r] = mul_f16_f32(ph[r >> 3][(r & 7) >> 1], r & 1, sx[r]);
+    pack16(dsv);
+    asm volatile("" : "+v"(sx));
+    return lraw;
   };
 
   // Step m starts once tiles m and m+1 are resident for every wave (tile m+1
@@ -574,13 +588,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     using SL = std::integral_constant<int, (u + 5) % NST>;
     using SNN = std::integral_constant<int, (u + 2) % NST>;
     sync_even(SL{}, t + 1);
-    const float lraw = lse_read(SNN{});
-    {  // -Delta of tile t+1 (negated in step t-1) for the next product phase
-      const f32x4* dsrc = reinterpret_cast<const f32x4*>(&Ss[SN::value][BQ + 4 * g]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) lsepf[m] = dsrc[2 * m];
-    }
-    b_v(ST{}, t);
+    const float lraw = b_v(SN{}, SNN{}, t);
     lse_write(SNN{}, lraw);
     __builtin_amdgcn_sched_barrier(0);
     m_phase(RoleB{}, SN{}, ST{});
