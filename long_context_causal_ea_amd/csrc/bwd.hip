@@ -386,7 +386,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   // operand being dO (A: dV) or Q (B: dK).  Operands through a register ring PF
   // products deep, pinned by scheduling groups (left to itself the compiler read
   // each operand right before its product and waited for it).
-  auto m_phase = [&](auto ROLE, auto CST, auto PST) {
+  auto m_phase = [&](auto ROLE, auto CST, auto PST, auto&& hook) {
     constexpr int R = decltype(ROLE)::value, cst = decltype(CST)::value, pst = decltype(PST)::value;
     constexpr int NSC = NKS, NAC = 2 * NDB, N = NSC + NAC, PF = 3;
     static_assert(PF <= NSC, "the ring starts inside the score products");
@@ -406,6 +406,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) lsepf[m] = lsrc[2 * m];
     }
+    hook();  // the tile loads, while the first reads are under way
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       if (i + PF < N) fr[i + PF] = rd(i + PF);
@@ -421,7 +423,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
         acc[j % NDB] = mfma32(as_bf16x8(fr[i]), pk[j / NDB], acc[j % NDB]);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // operands of the first PF products
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // product i
@@ -430,7 +431,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
       } else if (i + PF < N) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two reads of product i + PF
       }
-      if (R == 0 && i == 1) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the LSE reads
     }
     asm volatile("" : "+v"(sx));
     if constexpr (R == 0) {
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   // -Delta of tile t+1 (stage SN, negated one step earlier) for the next
   // product phase and, on wave 4, the raw statistic of tile t+2 (stage SNN)
   // that it converts afterwards (returned); the reads return in that order.
-  auto b_v = [&](auto SN, auto SNN, int t) {
+  auto b_v = [&](auto SN, auto SNN, int t, auto&& hook) {
     const u32x4* psrc8 = reinterpret_cast<const u32x4*>(&Ps[t & 1][kw][0][lane][0]);
     u32x4 ph[2];
     ph[0] = psrc8[0];
@@ -531,6 +531,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     }
     const float lraw = lse_read(SNN);
     __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);  // the seven reads in program order
+    __builtin_amdgcn_sched_barrier(0);
+    hook();  // the tile loads, while the reads are under way
+    __builtin_amdgcn_sched_barrier(0);
     float dsv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) dsv[r] = mul_f16_f32(ph[r >> 3][(r & 7) >> 1], r & 1, sx[r]);
@@ -542,23 +545,26 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   // Step m starts once tiles m and m+1 are resident for every wave (tile m+1
   // for the LSE conversion); then the loads of tile m+4 go into the stage tile
   // m-2 held (its last readers, the dV and dK products of tile m-2, ran in step
-  // m-1).
+  // m-1).  Each wave issues those loads right after the first LDS reads of the
+  // phase that follows the barrier (`hook`), so that their address work passes
+  // under the reads' latency.
   constexpr int AHEAD = 2;  // tiles in flight beyond the two needed
   static_assert(NST == 6, "loads run four tiles ahead in a ring of six stages");
   // Near the end no tile is loaded and the wave waits for all of its loads.
-  auto sync_even = [&](auto STAGE4, int m) {
+  auto sync_wait = [&](int m) {  // returns whether tile m + 4 is to be loaded
     __builtin_amdgcn_sched_barrier(0);
-    if (m + 4 < nt) {
+    const bool more = m + 4 < nt;
+    if (more) {
       wait_loads(std::integral_constant<int, AHEAD>{});
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      issue_next(decltype(STAGE4)::value, m);
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }
     __builtin_amdgcn_sched_barrier(0);
+    return more;
   };
   auto sync_plain = [&]() {
     __builtin_amdgcn_sched_barrier(0);
@@ -577,8 +583,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     using SL = std::integral_constant<int, (u + 5) % NST>;
     __builtin_amdgcn_sched_barrier(0);
     a_v(ST{}, t);
-    sync_even(SL{}, t + 1);
-    m_phase(RoleA{}, SN{}, ST{});
+    const bool more = sync_wait(t + 1);
+    m_phase(RoleA{}, SN{}, ST{}, [&]() { if (more) issue_next(SL::value, t + 1); });
     return t + 1 < nt;
   };
   auto b_step = [&](auto U, int t) {
@@ -587,11 +593,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     using SN = std::integral_constant<int, (u + 1) % NST>;
     using SL = std::integral_constant<int, (u + 5) % NST>;
     using SNN = std::integral_constant<int, (u + 2) % NST>;
-    sync_even(SL{}, t + 1);
-    const float lraw = b_v(SN{}, SNN{}, t);
+    const bool more = sync_wait(t + 1);
+    const float lraw = b_v(SN{}, SNN{}, t, [&]() { if (more) issue_next(SL::value, t + 1); });
     lse_write(SNN{}, lraw);
     __builtin_amdgcn_sched_barrier(0);
-    m_phase(RoleB{}, SN{}, ST{});
+    m_phase(RoleB{}, SN{}, ST{}, [] {});
     return t + 1 < nt;
   };
 
@@ -608,7 +614,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     // reloaded one) and drops it, so every product phase is the same straight
     // run of products.
     if (role == 0) {
-      m_phase(RoleA{}, S0{}, S0{});
+      m_phase(RoleA{}, S0{}, S0{}, [] {});
       sync_plain();
       {  // tile 0's LSE is converted before this barrier, after the first product phase read it
         const f32x4* lsrc = reinterpret_cast<const f32x4*>(&Ss[0][4 * g]);
@@ -632,7 +638,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) lsepf[m] = dsrc[2 * m];
       }
-      m_phase(RoleB{}, S0{}, S0{});
+      m_phase(RoleB{}, S0{}, S0{}, [] {});
       for (int t = 0;; t += 6) {
         if (!b_step(std::integral_constant<int, 0>{}, t)) break;
         if (!b_step(std::integral_constant<int, 1>{}, t + 1)) break;
