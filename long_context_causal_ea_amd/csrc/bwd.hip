@@ -458,13 +458,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     for (int kk = 0; kk < 2; ++kk) asm volatile("" : "+v"(pk[kk]));
   };
 
-  // A's vector phase for tile t (stage st): mask, P = exp2(S c - LSE2) (the LSE
+  // A's vector phase for tile t: mask, P = exp2(S c - LSE2) (the LSE
   // of the tile's rows, already in base-2 units (see to_log2), was read in the
   // product phase of the same step), published to
   // B as fp16 pairs, kept as bf16 packs for dV.  A barrier does not wait for
   // memory, so A waits for its LDS writes before the barrier that publishes them.
-  auto a_v = [&](auto ST, int t) {
-    constexpr int st = decltype(ST)::value;
+  auto a_v = [&](int t) {
     if (classify(t) == kPartial) {
       const int i0 = tile_of(t) * BQ;
 #pragma unroll
@@ -588,7 +587,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
     using SN = std::integral_constant<int, (u + 1) % NST>;
     using SL = std::integral_constant<int, (u + 5) % NST>;
     __builtin_amdgcn_sched_barrier(0);
-    a_v(ST{}, t);
+    a_v(t);
     const bool more = sync_wait(t + 1);
     m_phase(RoleA{}, SN{}, ST{}, [&]() { if (more) issue_next(SL::value, t + 1); });
     return t + 1 < nt;
