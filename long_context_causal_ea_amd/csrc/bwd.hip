@@ -312,7 +312,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   const int sstep = BQ * p.Hs, sjump = (tC0 - tA1 + 1) * BQ * p.Hs;
   const uint16_t* nq = qp;
   const uint16_t* no = op;
-  int ns = 0;  // statistics: first row times Hs
+  int ns = 0;  // statistics: first row times Hs (Sq*Hs < 2^29: the Delta launch's grid check bounds it)
   {
     const int r5 = __builtin_amdgcn_readfirstlane(tile_of(5 < nt ? 5 : 0) * BQ);
     nq += (long)r5 * p.rs;
