@@ -130,3 +130,68 @@ def test_rope_sweep(case):
     assert_lse("LSE", lse, ref["lse"])
     for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert_within(name, got, ref[name], bound[name])
+
+
+# ---- the keys split into parts, as a ring visits them -------------------------------------------------------
+def _slice_segments(seg, a, b):
+    """The (start, len) runs of rows [a, b) of the layout `seg`."""
+    out, row = [], 0
+    for s, n in zip(seg[0::2], seg[1::2]):
+        lo, hi = max(a, row), min(b, row + n)
+        if hi > lo:
+            out += [s + (lo - row), hi - lo]
+        row += n
+    return out or [0, 0]
+
+
+def _draw_split_cases(seed, count):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for D, B, sq, sk, causal, q_seg, k_seg, _, _ in _draw_cases(seed, count, rope=False):
+        cuts = sorted(int(x) for x in rng.integers(0, sk + 1, int(rng.choice([1, 2]))))  # parts may be empty
+        bounds = [0] + cuts + [sk]
+        order = [int(i) for i in rng.permutation(len(bounds) - 1)]
+        cases.append((D, B, sq, sk, causal, q_seg, k_seg, bounds, order))
+    return cases
+
+
+SPLIT = _draw_split_cases(20261205, 16) + [
+    # an empty part visited first (the forward writes -inf / 0, the first backward call still writes Delta),
+    # and an empty part visited between two others
+    (128, 1, 300, 200, True, [100, 300], [0, 200], [0, 0, 120, 200], [0, 1, 2]),
+    (64, 2, 257, 190, True, [0, 257], [0, 90, 300, 100], [0, 90, 90, 190], [2, 1, 0]),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", SPLIT, ids=[f"split{i}" for i in range(len(SPLIT))])
+def test_split_keys_sweep(case):
+    """The keys cut into parts visited in a random order: the first part's forward, the others merged into the
+    accumulator (ea_attn_fwd_merge); Delta written by the first backward call and reused; dQ accumulated over
+    the parts, each part's dK and dV written through row views of the whole tensors.  Against the oracle's
+    attention over all keys at once."""
+    D, B, sq, sk, causal, q_seg, k_seg, bounds, order = case
+    banner(f"split D={D} B={B} Sq={sq} Sk={sk} causal={causal} q_seg={q_seg} k_seg={k_seg} parts={bounds} "
+           f"order={order}")
+    H = 2
+    seed = 9000 + 10 * (sq + 3 * sk)
+    q, k, v, do = (synth.normal_draw((B, s, H, D), seed + i, 1.0, DEV).to(torch.bfloat16)
+                   for i, s in enumerate((sq, sk, sk, sq)))
+    f32 = lambda *s: torch.zeros(*s, device=DEV)
+    o, lse, delta = f32(B, sq, H, D), f32(B, sq, H), f32(B, sq, H)
+    dq, dk, dv = f32(B, sq, H, D), f32(B, sk, H, D), f32(B, sk, H, D)
+    parts = [(bounds[i], bounds[i + 1], _slice_segments(k_seg, bounds[i], bounds[i + 1])) for i in order]
+    for n, (a, b, seg) in enumerate(parts):
+        call = ea.ea_attn_fwd if n == 0 else ea.ea_attn_fwd_merge
+        call(q, k[:, a:b], v[:, a:b], o, lse, q_seg, seg, causal)
+    for n, (a, b, seg) in enumerate(parts):
+        ea.ea_attn_bwd(q, k[:, a:b], v[:, a:b], o, do, lse, delta, dq, dk[:, a:b], dv[:, a:b], q_seg, seg, causal,
+                       delta_ready=n > 0)
+    torch.cuda.synchronize()
+    pq, pk, scale = seg_positions(q_seg), seg_positions(k_seg), scale_of(D)
+    ref = oracle.attn_bwd_heads(q, k, v, do, pq, pk, causal, scale)
+    bound = rounding_bounds(q, k, v, do, pq, pk, causal, scale, ref)
+    assert_within("O", o, ref["o"], bound["o"])
+    assert_lse("LSE", lse, ref["lse"])
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_within(name, got, ref[name], bound[name])
