@@ -75,6 +75,23 @@ def test_drawn_cases_are_valid():
             assert all(s >= 0 and s + ln <= TOP for s, ln in zip(seg[0::2], seg[1::2]))
 
 
+def test_drawn_cases_cover_the_features():
+    """The fixed draws include what the module docstring promises: both head dimensions and masks, batches of
+    two, two-run layouts with the second run first (on the query and on the key side), positions near 2^31,
+    counts a row either side of a tile boundary, bf16 outputs, and each rotary base."""
+    def two_runs_reversed(seg):
+        return len(seg) == 4 and seg[2] < seg[0]
+    for cases in (DENSE, ROPE):
+        assert {c[0] for c in cases} == {64, 128} and {c[4] for c in cases} == {True, False}
+        assert any(c[1] == 2 for c in cases)
+    assert any(two_runs_reversed(c[5]) for c in DENSE) and any(two_runs_reversed(c[6]) for c in DENSE)
+    assert any(c[5][0] > TOP // 2 for c in DENSE) and any(c[5][0] > TOP // 2 for c in ROPE)
+    assert any(n % 32 in (1, 31) for c in DENSE for n in (c[2], c[3]))
+    assert any(c[7] == torch.bfloat16 for c in DENSE)
+    assert {c[8] for c in ROPE} == {1e4, 1e6, 1e9}
+    assert any(len(b) == 4 for *_, b, _ in SPLIT) and any(b[i] == b[i + 1] for *_, b, _ in SPLIT for i in range(len(b) - 1))
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("case", DENSE, ids=[f"dense{i}" for i in range(len(DENSE))])
 def test_dense_sweep(case):
